@@ -1,0 +1,18 @@
+"""MI355X-native MoE expert layer: routing, sentinel-aware offsets, permute,
+grouped GEMMs with fused SiLU*up, and combine, as hand-written HIP for gfx950
+behind the C ABI in ``include/moe.h``.
+
+``ops`` holds torch-tensor wrappers (argument marshalling only); ``_lib``
+loads ``libmoe.so``; ``build`` compiles it.
+"""
+
+from ._lib import MoeKernels, load  # noqa: F401
+from .ops import (  # noqa: F401
+    build_offsets,
+    forward,
+    forward_workspace_bytes,
+    grouped_gemm,
+    permute,
+    route_topk,
+    unpermute_combine,
+)

@@ -1,0 +1,299 @@
+// api.hip -- the extern "C" entry points declared in include/moe.h.
+//
+// Every entry point validates its arguments on the host before any launch,
+// enqueues work on the caller's stream, never synchronises, allocates nothing
+// and keeps no pointer.  Errors come back as moe_status_t plus a thread-local
+// message; no C++ exception crosses the boundary.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+#include "moe.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(moe_dtype_t d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
+
+bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_FP8_E4M3; }
+
+constexpr long long kMaxRows = 0x7fffffffLL;
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define MOE_REQUIRE(cond, ...) \
+  do {                         \
+    if (!(cond)) return fail(MOE_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+moe_status_t check_experts(int32_t E, int32_t k) {
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  MOE_REQUIRE(k >= 1 && k <= MOE_MAX_TOPK && k <= E, "k=%d outside [1, min(E, %d)]", k, MOE_MAX_TOPK);
+  return MOE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct FwdLayout {
+  size_t ids, w, offsets, sorted, rowpos, offws, xp, xps, h, hs, y, total;
+};
+
+FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dtype_t w_dtype) {
+  const long long R = T * k;
+  const bool fp8 = w_dtype == MOE_FP8_E4M3;
+  const size_t e_act = w_dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);  // x_perm and h
+  const size_t e_y = w_dtype == MOE_F32 ? 4 : 2;
+  FwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.ids = take(R * 4);
+  L.w = take(R * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted = take(R * 4);
+  L.rowpos = take(R * 4);
+  L.offws = take(moe::build_offsets_workspace_bytes(R, E));
+  L.xp = take(R * H * e_act);
+  L.xps = take(fp8 ? R * (H / 128) * 4 : 0);
+  L.h = take(R * I * e_act);
+  L.hs = take(fp8 ? R * (I / 128) * 4 : 0);
+  L.y = take(R * H * e_y);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status_t moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                            int64_t num_valid_rows, int32_t renormalize, int32_t* topk_ids,
+                            float* topk_weights, void* stream) {
+  if (moe_status_t s = check_experts(E, k)) return s;
+  MOE_REQUIRE(T >= 0 && T * k <= kMaxRows, "T=%lld out of range", (long long)T);
+  if (T == 0) return ok();
+  MOE_REQUIRE(logits && topk_ids && topk_weights, "null pointer argument");
+  return launched(moe::launch_route_topk(logits, (int)T, E, k, num_valid_rows, renormalize ? 1 : 0,
+                                         topk_ids, topk_weights, as_stream(stream)),
+                  "route_topk");
+}
+
+size_t moe_build_offsets_workspace(int64_t R, int32_t E) {
+  if (R < 0 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  return moe::build_offsets_workspace_bytes(R, E);
+}
+
+moe_status_t moe_build_offsets(const int32_t* topk_ids, int64_t R, int32_t E, int32_t* offsets,
+                               int32_t* sorted_rows, int32_t* row_pos, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  MOE_REQUIRE(R >= 0 && R <= kMaxRows, "R=%lld out of range", (long long)R);
+  MOE_REQUIRE(offsets, "offsets is null");
+  MOE_REQUIRE(R == 0 || (topk_ids && sorted_rows && row_pos), "null pointer argument");
+  const size_t need = moe::build_offsets_workspace_bytes(R, E);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  return launched(moe::launch_build_offsets(topk_ids, (int)R, E, offsets, sorted_rows, row_pos,
+                                            workspace, as_stream(stream)),
+                  "build_offsets");
+}
+
+moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t H, int32_t k,
+                         const int32_t* sorted_rows, const int32_t* offsets, int32_t E, int64_t R,
+                         void* x_perm, moe_dtype_t perm_dtype, float* x_perm_scales,
+                         void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  MOE_REQUIRE(k >= 1 && k <= MOE_MAX_TOPK, "k=%d outside [1, %d]", k, MOE_MAX_TOPK);
+  MOE_REQUIRE(T >= 0 && R >= 0 && R <= kMaxRows && H > 0 && H <= kMaxRows, "bad sizes");
+  MOE_REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, "x_dtype must be MOE_F32 or MOE_BF16");
+  if (R == 0) return ok();
+  MOE_REQUIRE(x && sorted_rows && offsets && x_perm, "null pointer argument");
+  MOE_REQUIRE(aligned16(x) && aligned16(x_perm), "x and x_perm must be 16-byte aligned");
+  MOE_REQUIRE((H * esize(x_dtype)) % 16 == 0, "rows of x must be a multiple of 16 bytes");
+  if (perm_dtype == x_dtype)
+    return launched(moe::launch_permute_copy(x, (int)T, (int)(H * esize(x_dtype)), k, sorted_rows, offsets,
+                                             E, (int)R, x_perm, as_stream(stream)),
+                    "permute");
+  if (perm_dtype == MOE_FP8_E4M3 && x_dtype == MOE_BF16) {
+    MOE_REQUIRE(H % 128 == 0, "fp8 permute needs H %% 128 == 0");
+    MOE_REQUIRE(x_perm_scales, "x_perm_scales is null");
+    return launched(moe::launch_permute_quant(x, (int)T, (int)H, k, sorted_rows, offsets, E, (int)R, x_perm,
+                                              x_perm_scales, as_stream(stream)),
+                    "permute_quant");
+  }
+  return fail(MOE_ERR_UNSUPPORTED, "permute from dtype %d to dtype %d", (int)x_dtype, (int)perm_dtype);
+}
+
+moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* B,
+                              const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
+                              int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
+                              void* C, moe_dtype_t c_dtype, float* c_scales, void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  MOE_REQUIRE(valid_dtype(ab_dtype) && valid_dtype(c_dtype), "bad dtype");
+  MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
+  MOE_REQUIRE(M_rows >= 0 && M_rows <= kMaxRows && N > 0 && N <= kMaxRows && K > 0 &&
+                  K * esize(ab_dtype) <= kMaxRows,
+              "bad sizes");
+  const bool silu = epi == MOE_EPI_SILU_MUL;
+  MOE_REQUIRE(!silu || N % 2 == 0, "SiLU*up needs an even N");
+  const long long N_out = silu ? N / 2 : N;
+  MOE_REQUIRE((K * esize(ab_dtype)) % 16 == 0, "rows of A and B must be a multiple of 16 bytes");
+  MOE_REQUIRE((N_out * esize(c_dtype)) % 16 == 0, "rows of C must be a multiple of 16 bytes");
+  if (ab_dtype == MOE_FP8_E4M3) {
+    MOE_REQUIRE(K % 128 == 0 && N % 128 == 0, "fp8 GEMM needs N and K multiples of 128");
+    MOE_REQUIRE(a_scales && b_scales, "fp8 GEMM needs a_scales and b_scales");
+    MOE_REQUIRE(!silu || N_out % 128 == 0, "fp8 SiLU*up needs N/2 %% 128 == 0");
+  }
+  if (c_dtype == MOE_FP8_E4M3) {
+    if (!(ab_dtype == MOE_FP8_E4M3 && silu))
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 output is supported for fp8 operands with SiLU*up");
+    MOE_REQUIRE(N_out % 128 == 0 && c_scales, "fp8 output needs N_out %% 128 == 0 and c_scales");
+  }
+  if (M_rows == 0) return ok();
+  MOE_REQUIRE(A && B && offsets && C, "null pointer argument");
+  MOE_REQUIRE(aligned16(A) && aligned16(B) && aligned16(C), "A, B and C must be 16-byte aligned");
+  moe::GemmLaunch p{};
+  p.A = A;
+  p.a_scales = a_scales;
+  p.B = B;
+  p.b_scales = b_scales;
+  p.ab_dtype = ab_dtype;
+  p.offsets = offsets;
+  p.E = E;
+  p.M_rows = M_rows;
+  p.N = N;
+  p.K = K;
+  p.silu = silu;
+  p.C = C;
+  p.c_dtype = c_dtype;
+  p.c_scales = c_scales;
+  return launched(moe::launch_grouped_gemm(p, as_stream(stream)), "grouped_gemm");
+}
+
+moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int32_t* row_pos,
+                                   const float* topk_weights, const int32_t* offsets, int32_t E,
+                                   int64_t T, int64_t H, int32_t k, void* out,
+                                   moe_dtype_t out_dtype, void* stream) {
+  if (moe_status_t s = check_experts(E, k)) return s;
+  MOE_REQUIRE(T >= 0 && T * k <= kMaxRows && H > 0 && H <= kMaxRows, "bad sizes");
+  MOE_REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_BF16, "y_dtype must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(out_dtype == MOE_F32 || out_dtype == MOE_BF16, "out_dtype must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE((H * esize(y_dtype)) % 16 == 0 && H % 4 == 0, "rows of y must be a multiple of 16 bytes");
+  if (T == 0) return ok();
+  MOE_REQUIRE(y && row_pos && topk_weights && offsets && out, "null pointer argument");
+  MOE_REQUIRE(aligned16(y) && aligned16(out), "y and out must be 16-byte aligned");
+  return launched(moe::launch_combine(y, y_dtype == MOE_BF16, row_pos, topk_weights, offsets, E, (int)T,
+                                      (int)H, k, out, out_dtype == MOE_BF16, as_stream(stream)),
+                  "unpermute_combine");
+}
+
+size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                             moe_dtype_t w_dtype) {
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK ||
+      !valid_dtype(w_dtype))
+    return 0;
+  return fwd_layout(T, H, I, E, k, w_dtype).total;
+}
+
+moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router_logits,
+                         const void* w13, const float* w13_scales, const void* w2,
+                         const float* w2_scales, moe_dtype_t w_dtype, int64_t T, int64_t H,
+                         int64_t I, int32_t E, int32_t k, int64_t num_valid_rows,
+                         int32_t renormalize, void* out, moe_dtype_t out_dtype, moe_aux_t* aux,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status_t s = check_experts(E, k)) return s;
+  MOE_REQUIRE(valid_dtype(w_dtype), "bad w_dtype");
+  MOE_REQUIRE(T >= 0 && T * k <= kMaxRows && H > 0 && I > 0 && H <= kMaxRows && I <= kMaxRows,
+              "bad sizes");
+  const bool fp8 = w_dtype == MOE_FP8_E4M3;
+  MOE_REQUIRE(x_dtype == (w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16),
+              "x_dtype must be MOE_F32 for f32 weights and MOE_BF16 otherwise");
+  MOE_REQUIRE(out_dtype == MOE_F32 || out_dtype == MOE_BF16, "out_dtype must be MOE_F32 or MOE_BF16");
+  if (fp8) {
+    MOE_REQUIRE(H % 128 == 0 && I % 128 == 0, "fp8 layer needs H and I multiples of 128");
+    MOE_REQUIRE(w13_scales && w2_scales, "fp8 layer needs weight scales");
+  } else {
+    MOE_REQUIRE((H * esize(w_dtype)) % 16 == 0 && (I * esize(w_dtype)) % 16 == 0,
+                "H and I rows must be multiples of 16 bytes");
+  }
+  const FwdLayout L = fwd_layout(T, H, I, E, k, w_dtype);
+  if (T > 0) {
+    MOE_REQUIRE(x && router_logits && w13 && w2 && out, "null pointer argument");
+    MOE_REQUIRE(aligned16(x) && aligned16(w13) && aligned16(w2) && aligned16(out),
+                "x, weights and out must be 16-byte aligned");
+  }
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  MOE_REQUIRE(aligned16(workspace), "workspace must be 16-byte aligned");
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* ids = (aux && aux->topk_ids) ? aux->topk_ids : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = (aux && aux->topk_weights) ? aux->topk_weights : reinterpret_cast<float*>(ws + L.w);
+  int32_t* offs = (aux && aux->offsets) ? aux->offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = (aux && aux->sorted_rows) ? aux->sorted_rows : reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* rowpos = (aux && aux->row_pos) ? aux->row_pos : reinterpret_cast<int32_t*>(ws + L.rowpos);
+  const long long R = T * k;
+
+  moe_status_t s;
+  if ((s = moe_route_topk(router_logits, T, E, k, num_valid_rows, renormalize, ids, wts, stream)))
+    return s;
+  if ((s = moe_build_offsets(ids, R, E, offs, sorted, rowpos, ws + L.offws,
+                             moe::build_offsets_workspace_bytes(R, E), stream)))
+    return s;
+  if (T == 0) return ok();
+  const moe_dtype_t act = fp8 ? MOE_FP8_E4M3 : w_dtype;
+  const moe_dtype_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+  float* xps = fp8 ? reinterpret_cast<float*>(ws + L.xps) : nullptr;
+  float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
+  if ((s = moe_permute(x, x_dtype, T, H, k, sorted, offs, E, R, ws + L.xp, act, xps, stream)))
+    return s;
+  if ((s = moe_grouped_gemm(ws + L.xp, xps, w13, w13_scales, w_dtype, offs, E, R, 2 * I, H,
+                            MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream)))
+    return s;
+  if ((s = moe_grouped_gemm(ws + L.h, hs, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
+                            ws + L.y, ydt, nullptr, stream)))
+    return s;
+  return moe_unpermute_combine(ws + L.y, ydt, rowpos, wts, offs, E, T, H, k, out, out_dtype, stream);
+}
+
+}  // extern "C"

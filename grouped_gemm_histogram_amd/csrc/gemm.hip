@@ -1,0 +1,517 @@
+// gemm.hip -- persistent grouped GEMM over expert segments on CDNA4 matrix cores.
+//
+// For each expert e and permuted row p in [offsets[e], offsets[e+1]):
+//     acc[p, n] = sum_k A[p, k] * B[e, n, k]          (fp32 accumulate)
+// followed by one of two epilogues: store acc, or store silu(gate) * up where
+// gate and up are B rows n and N/2 + n.  This is the grouped GEMM with equal N
+// and K per group (group_gemm_same_nk) and the SiLU(fc1_1) * fc1_2 step of the
+// LlamaFactory PR #10481 write-up, section 1; the grouped_mm expert backend of
+// "트랜스포머에서 전문가 혼합 (MoEs)".  Only rows below offsets[E] get tiles, and
+// rows [offsets[E], M_rows) of C are written as zeros (the transformers PR
+// #45621 write-up: section 2 excludes sentinel rows from the work, section 3
+// traces a NaN to sentinel outputs left unwritten).
+//
+// Design (gfx950):
+//  * Persistent grid of (#CU x occupancy) workgroups.  Every workgroup reads
+//    offsets from device memory and builds the per-expert m-tile prefix in
+//    LDS, so the launch needs no host knowledge of the expert loads.
+//  * Tile order: expert-major, then n-tile, then m-tile fastest, so the few
+//    m-tiles sharing one weight panel run back to back.  The tile index is
+//    remapped so that consecutive tiles go to workgroups of the same XCD
+//    (workgroup w is dispatched to XCD w % 8): tiles that share a weight
+//    panel and an activation panel meet in that XCD's L2.
+//  * K is walked in 128-byte slices (64 bf16 / 32 f32 / 128 e4m3 per row),
+//    double-buffered in LDS through registers: the next slice's global loads
+//    are in flight while the current one feeds the MFMAs.  Each LDS row is
+//    128 bytes = eight 16-byte chunks stored XOR-swizzled, so that the
+//    16 rows read by one MFMA operand fetch hit distinct banks.
+//  * MFMA operand roles are swapped: weight rows are the 16-row src0 operand
+//    and activation rows the src1 operand, so each lane's results are output
+//    columns of one activation row.  Inside each wave the weight rows are
+//    placed in LDS in an order that makes every lane's columns contiguous
+//    (4 x subtiles), which turns the epilogue into 16-byte row stores.
+//  * bf16: v_mfma_f32_16x16x32_bf16; f32: v_mfma_f32_16x16x4_f32; e4m3:
+//    v_mfma_f32_16x16x128_f8f6f4 with one 128-deep MFMA per 128x128 weight
+//    block, whose fp32 result is scaled by (activation scale x weight block
+//    scale) and added to the accumulator.
+//  * e4m3 output (h of the fp8 layer): the 128 columns of a tile form one
+//    quantisation group; its |max| is reduced across lanes and waves, then
+//    scale = amax / 448 and codes = RNE(value / scale).
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+enum class AbType { F32, BF16, FP8 };
+enum class CType { F32, BF16, FP8 };
+
+template <AbType T> struct AbTraits;
+template <> struct AbTraits<AbType::BF16> {
+  static constexpr int kEsize = 2, kSteps = 2, kChunksPerLane = 1;
+};
+template <> struct AbTraits<AbType::F32> {
+  static constexpr int kEsize = 4, kSteps = 2, kChunksPerLane = 1;
+};
+template <> struct AbTraits<AbType::FP8> {
+  static constexpr int kEsize = 1, kSteps = 1, kChunksPerLane = 2;
+};
+
+struct GemmArgs {
+  const uint8_t* A;
+  const float* a_scales;
+  const uint8_t* B;
+  const float* b_scales;
+  const int* offsets;
+  int E;
+  int M_rows;
+  int N;        // B rows per expert
+  int K;        // elements
+  uint8_t* C;
+  float* c_scales;
+  int N_out;    // columns of C
+  int n_tiles;  // ceil(N_out / BN_out)
+};
+
+constexpr int kSliceBytes = 128;  // bytes of K per LDS row
+constexpr int kMaxExperts = 1024;
+
+// Swizzle of the 16-byte chunk index within a 128-byte LDS row.  Rows r and
+// r+8 differ in the low bit, so 16 consecutive rows read at one logical chunk
+// land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+struct GemmCfg {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kWRows = BM / WM;            // activation rows per wave
+  static constexpr int kSM = kWRows / 16;           // activation subtiles per wave
+  static constexpr int kWNB = BNB / WN;             // weight rows per wave
+  static constexpr int kSNB = kWNB / 16;            // weight subtiles per wave
+  static constexpr int kSNO = SILU ? kSNB / 2 : kSNB;  // output subtiles per wave
+  static constexpr int kBNOut = SILU ? BNB / 2 : BNB;  // output columns per tile
+  static constexpr int kWNOut = kBNOut / WN;        // output columns per wave (= 16 kSNO)
+  static constexpr int kTileBytes = (BM + BNB) * kSliceBytes;
+  static constexpr int kAIters = BM * 8 / kThreads;
+  static constexpr int kBIters = BNB * 8 / kThreads;
+  static_assert(BM % (16 * WM) == 0 && BNB % (16 * WN) == 0, "tile/wave mismatch");
+  static_assert(!SILU || kSNB % 2 == 0, "SiLU needs gate and up subtiles in every wave");
+  static_assert((BM * 8) % kThreads == 0 && (BNB * 8) % kThreads == 0, "loader mismatch");
+  static_assert(kThreads / 8 % 16 == 0, "loader rows must keep the swizzle phase");
+  static_assert(CT != CType::FP8 || (SILU && kBNOut == 128), "fp8 output needs 128-column tiles");
+};
+
+// Output column (within the wave's slab) held by MFMA row ii of subtile s.
+template <int SN>
+__device__ __forceinline__ int slab_col(int s, int ii) {
+  return 4 * SN * (ii >> 2) + 4 * s + (ii & 3);
+}
+
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN>;
+  using Tr = AbTraits<AB>;
+  constexpr int THREADS = Cfg::kThreads;
+  constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][Cfg::kTileBytes];
+  __shared__ int s_mt_pre[kMaxExperts + 1];
+  __shared__ float s_red[(CT == CType::FP8) ? WN * BM : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int ii = lane & 15;   // MFMA row/column index of this lane
+  const int g = lane >> 4;    // MFMA k-group of this lane
+  const int E = args.E;
+  const int* __restrict__ offsets = args.offsets;
+  // offsets as read from memory, clamped to [0, M_rows] so that no row index
+  // can leave A or C even for inconsistent input
+  auto off_at = [&](int e) { return min(max(offsets[e], 0), args.M_rows); };
+
+  // ---- per-expert m-tile prefix (wave 0, serial per lane + shuffle scan)
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) local += (max(off_at(e + 1) - off_at(e), 0) + BM - 1) / BM;
+    }
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - local;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        s_mt_pre[e] = run;
+        run += (max(off_at(e + 1) - off_at(e), 0) + BM - 1) / BM;
+      }
+    }
+    if (lane == 63) s_mt_pre[E] = incl;
+  }
+  __syncthreads();
+
+  const int total_mt = s_mt_pre[E];
+  const int n_tiles = args.n_tiles;
+  const int total_tiles = total_mt * n_tiles;
+  const int G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (int)((blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int)blockIdx.x;
+
+  const int K = args.K;
+  const int k_bytes = K * Tr::kEsize;
+  const int KT = (k_bytes + kSliceBytes - 1) / kSliceBytes;
+  const int N_out = args.N_out;
+  const long long lda = k_bytes;
+
+  // loader geometry: thread owns chunk (tid & 7) of rows (tid >> 3) + i * THREADS/8
+  const int ld_ch = tid & 7;
+  const int ld_row0 = tid >> 3;
+  constexpr int LD_ROW_STEP = THREADS / 8;
+  const int ld_lds = ld_row0 * kSliceBytes + ((ld_ch ^ swz(ld_row0)) << 4);
+
+  // fragment read geometry
+  const int rd_swz = swz(ii);
+
+  for (int tile = slot; tile < total_tiles; tile += G) {
+    // ---- decode tile -> (expert, n-tile, m-tile)
+    const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
+    int lo = 0, hi = E;             // largest e with s_mt_pre[e] <= q
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_mt_pre[mid] <= q) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int mt_e = s_mt_pre[e + 1] - s_mt_pre[e];
+    const int local = tile - s_mt_pre[e] * n_tiles;
+    const int nt = local / mt_e;
+    const int ml = local - nt * mt_e;
+    const int seg_end = off_at(e + 1);
+    const int m0 = off_at(e) + ml * BM;
+    const int rows_valid = min(BM, seg_end - m0);
+    const int n0 = nt * Cfg::kBNOut;
+
+    // ---- global source rows of this thread's chunks
+    const uint8_t* a_src[Cfg::kAIters];
+#pragma unroll
+    for (int i = 0; i < Cfg::kAIters; ++i) {
+      const int r = min(m0 + ld_row0 + i * LD_ROW_STEP, seg_end - 1);
+      a_src[i] = args.A + (long long)r * lda + ld_ch * 16;
+    }
+    const uint8_t* b_src[Cfg::kBIters];
+    const uint8_t* b_exp = args.B + (long long)e * args.N * lda;
+#pragma unroll
+    for (int i = 0; i < Cfg::kBIters; ++i) {
+      const int qrow = ld_row0 + i * LD_ROW_STEP;          // LDS row within the weight tile
+      int half = 0, qq = qrow;
+      if constexpr (SILU) {
+        half = qrow / Cfg::kBNOut;
+        qq = qrow - half * Cfg::kBNOut;
+      }
+      constexpr int SLAB = Cfg::kWNOut;
+      const int within = qq % SLAB;
+      const int col = n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15);
+      const int colc = min(col, N_out - 1);
+      b_src[i] = b_exp + (long long)(half * N_out + colc) * lda + ld_ch * 16;
+    }
+
+    uint4 a_reg[Cfg::kAIters], b_reg[Cfg::kBIters];
+    auto load_slice = [&](int kt) {
+      const int kb = kt * kSliceBytes + ld_ch * 16;
+      const bool in = kb < k_bytes;
+#pragma unroll
+      for (int i = 0; i < Cfg::kAIters; ++i)
+        a_reg[i] = in ? *reinterpret_cast<const uint4*>(a_src[i] + kt * kSliceBytes)
+                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < Cfg::kBIters; ++i)
+        b_reg[i] = in ? *reinterpret_cast<const uint4*>(b_src[i] + kt * kSliceBytes)
+                      : make_uint4(0, 0, 0, 0);
+    };
+    auto store_slice = [&](int buf) {
+      uint8_t* base = smem[buf];
+#pragma unroll
+      for (int i = 0; i < Cfg::kAIters; ++i)
+        *reinterpret_cast<uint4*>(base + ld_lds + i * LD_ROW_STEP * kSliceBytes) = a_reg[i];
+#pragma unroll
+      for (int i = 0; i < Cfg::kBIters; ++i)
+        *reinterpret_cast<uint4*>(base + BM * kSliceBytes + ld_lds + i * LD_ROW_STEP * kSliceBytes) =
+            b_reg[i];
+    };
+
+    f32x4 acc[SM][SNB];
+#pragma unroll
+    for (int t = 0; t < SM; ++t)
+#pragma unroll
+      for (int s = 0; s < SNB; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // fp8: weight block-scale rows of this wave (gate / up halves, or the single slab)
+    const float* bsc = nullptr;
+    int nb_half[2] = {0, 0};
+    const int KB = K / 128;
+    if constexpr (AB == AbType::FP8) {
+      const int NB = args.N / 128;
+      if constexpr (SILU) {
+        nb_half[0] = (n0 + wn * Cfg::kWNOut) / 128;
+        nb_half[1] = (N_out + n0 + wn * Cfg::kWNOut) / 128;
+      } else {
+        nb_half[0] = nb_half[1] = (n0 + wn * Cfg::kWNB) / 128;
+      }
+      nb_half[0] = min(nb_half[0], NB - 1);
+      nb_half[1] = min(nb_half[1], NB - 1);
+      bsc = args.b_scales + (long long)e * NB * KB;
+    }
+
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) load_slice(kt + 1);
+      const uint8_t* sA = smem[cur] + (wm * Cfg::kWRows) * kSliceBytes;
+      const uint8_t* sB = smem[cur] + BM * kSliceBytes;
+
+      float afac[SM][2];
+      if constexpr (AB == AbType::FP8) {
+        const float sb0 = bsc[nb_half[0] * KB + kt];
+        const float sb1 = bsc[nb_half[1] * KB + kt];
+#pragma unroll
+        for (int t = 0; t < SM; ++t) {
+          const int r = min(m0 + wm * Cfg::kWRows + 16 * t + ii, seg_end - 1);
+          const float sa = args.a_scales[(long long)r * KB + kt];
+          afac[t][0] = sa * sb0;
+          afac[t][1] = sa * sb1;
+        }
+      }
+
+#pragma unroll
+      for (int step = 0; step < Tr::kSteps; ++step) {
+        uint4 af[SM][Tr::kChunksPerLane], wf[SNB][Tr::kChunksPerLane];
+#pragma unroll
+        for (int c = 0; c < Tr::kChunksPerLane; ++c) {
+          const int ch = (Tr::kChunksPerLane == 1) ? (step * 4 + g) : (2 * g + c);
+          const int coff = (ch ^ rd_swz) << 4;
+#pragma unroll
+          for (int t = 0; t < SM; ++t)
+            af[t][c] = *reinterpret_cast<const uint4*>(sA + (16 * t + ii) * kSliceBytes + coff);
+#pragma unroll
+          for (int s = 0; s < SNB; ++s) {
+            int wrow;
+            if constexpr (SILU) {
+              const int half = s / SNO, ss = s - half * SNO;
+              wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
+            } else {
+              wrow = wn * Cfg::kWNB + 16 * s + ii;
+            }
+            wf[s][c] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < SM; ++t) {
+#pragma unroll
+          for (int s = 0; s < SNB; ++s) {
+            if constexpr (AB == AbType::BF16) {
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, wf[s][0]), __builtin_bit_cast(bf16x8, af[t][0]),
+                  acc[t][s], 0, 0, 0);
+            } else if constexpr (AB == AbType::F32) {
+              const float4 w4 = __builtin_bit_cast(float4, wf[s][0]);
+              const float4 a4 = __builtin_bit_cast(float4, af[t][0]);
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.x, a4.x, acc[t][s], 0, 0, 0);
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.y, a4.y, acc[t][s], 0, 0, 0);
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.z, a4.z, acc[t][s], 0, 0, 0);
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.w, a4.w, acc[t][s], 0, 0, 0);
+            } else {
+              const i32x8 wv = {(int)wf[s][0].x, (int)wf[s][0].y, (int)wf[s][0].z, (int)wf[s][0].w,
+                                (int)wf[s][1].x, (int)wf[s][1].y, (int)wf[s][1].z, (int)wf[s][1].w};
+              const i32x8 av = {(int)af[t][0].x, (int)af[t][0].y, (int)af[t][0].z, (int)af[t][0].w,
+                                (int)af[t][1].x, (int)af[t][1].y, (int)af[t][1].z, (int)af[t][1].w};
+              const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  wv, av, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+              const float f = afac[t][SILU ? (s / SNO) : 0];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(part[r], f, acc[t][s][r]);
+            }
+          }
+        }
+      }
+
+      if (kt + 1 < KT) store_slice(cur ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of rows 16t + ii
+    const int cbase = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
+#pragma unroll
+    for (int t = 0; t < SM; ++t) {
+      const int rloc = wm * Cfg::kWRows + 16 * t + ii;
+      const bool row_ok = rloc < rows_valid;
+      const long long m = (long long)m0 + rloc;
+      float v[4 * SNO];
+#pragma unroll
+      for (int s = 0; s < SNO; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          v[4 * s + r] = SILU ? silu_mul(acc[t][s][r], acc[t][SNO + s][r]) : acc[t][s][r];
+
+      if constexpr (CT == CType::FP8) {
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4 * SNO; ++i) am = fmaxf(am, fabsf(v[i]));
+        am = fmaxf(am, __shfl_xor(am, 16, 64));
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        if (g == 0) s_red[wn * BM + rloc] = am;
+        __syncthreads();
+        float amax = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, s_red[w2 * BM + rloc]);
+        __syncthreads();
+        const float scale = (amax == 0.f) ? 1.f : amax / 448.f;
+        if (row_ok && cbase < N_out) {
+          uint32_t wd[SNO];
+#pragma unroll
+          for (int s = 0; s < SNO; ++s)
+            wd[s] = cvt_e4m3x2(clamp448(v[4 * s] / scale), clamp448(v[4 * s + 1] / scale)) |
+                    (cvt_e4m3x2(clamp448(v[4 * s + 2] / scale), clamp448(v[4 * s + 3] / scale)) << 16);
+          uint8_t* dst = args.C + m * N_out + cbase;
+          static_assert(SNO == 4, "fp8 epilogue writes 16 codes per lane");
+          *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          if (wn == 0 && g == 0) args.c_scales[m * (N_out / 128) + n0 / 128] = scale;
+        }
+      } else if constexpr (CT == CType::BF16) {
+        if (row_ok) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(args.C) + m * N_out + cbase;
+          if constexpr (SNO == 1) {
+            if (cbase < N_out)
+              *reinterpret_cast<uint2*>(dst) =
+                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          } else {
+#pragma unroll
+            for (int u = 0; u < SNO / 2; ++u)
+              if (cbase + 8 * u < N_out)
+                *reinterpret_cast<uint4*>(dst + 8 * u) =
+                    make_uint4(pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]),
+                               pack_bf16x2(v[8 * u + 4], v[8 * u + 5]),
+                               pack_bf16x2(v[8 * u + 6], v[8 * u + 7]));
+          }
+        }
+      } else {
+        if (row_ok) {
+          float* dst = reinterpret_cast<float*>(args.C) + m * N_out + cbase;
+#pragma unroll
+          for (int s = 0; s < SNO; ++s)
+            if (cbase + 4 * s < N_out)
+              *reinterpret_cast<float4*>(dst + 4 * s) =
+                  make_float4(v[4 * s], v[4 * s + 1], v[4 * s + 2], v[4 * s + 3]);
+        }
+      }
+    }
+  }
+
+  // ---- sentinel rows [offsets[E], M_rows) of C: exact zeros (fp8 scales: 1.0)
+  {
+    constexpr int kCEsize = (CT == CType::F32) ? 4 : (CT == CType::BF16 ? 2 : 1);
+    const long long V = off_at(E);
+    const long long rows = (long long)args.M_rows - V;
+    if (rows > 0) {
+      const long long row_bytes = (long long)N_out * kCEsize;
+      const long long n16 = rows * row_bytes / 16;
+      uint4* base = reinterpret_cast<uint4*>(args.C + V * row_bytes);
+      for (long long i = (long long)blockIdx.x * THREADS + tid; i < n16; i += (long long)G * THREADS)
+        base[i] = make_uint4(0, 0, 0, 0);
+      if constexpr (CT == CType::FP8) {
+        const long long ns = rows * (N_out / 128);
+        float* sb = args.c_scales + V * (N_out / 128);
+        for (long long i = (long long)blockIdx.x * THREADS + tid; i < ns; i += (long long)G * THREADS)
+          sb[i] = 1.0f;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- host side
+
+namespace {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN>;
+  GemmArgs a = a0;
+  a.n_tiles = (a.N_out + Cfg::kBNOut - 1) / Cfg::kBNOut;
+  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN>;
+  static const int per_cu = [&] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::kThreads, 0) != hipSuccess || n <= 0)
+      n = 1;
+    return n;
+  }();
+  const int grid = device_cu_count() * per_cu;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
+  GemmArgs a{};
+  a.A = static_cast<const uint8_t*>(p.A);
+  a.a_scales = p.a_scales;
+  a.B = static_cast<const uint8_t*>(p.B);
+  a.b_scales = p.b_scales;
+  a.offsets = p.offsets;
+  a.E = p.E;
+  a.M_rows = (int)p.M_rows;
+  a.N = (int)p.N;
+  a.K = (int)p.K;
+  a.C = static_cast<uint8_t*>(p.C);
+  a.c_scales = p.c_scales;
+  a.N_out = p.silu ? (int)(p.N / 2) : (int)p.N;
+
+  // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
+  if (p.ab_dtype == 1) {
+    if (p.silu) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, 128, 128, 2, 2>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, true, 128, 128, 2, 2>(a, stream);
+    }
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, 128, 128, 2, 2>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, 128, 128, 2, 2>(a, stream);
+  }
+  if (p.ab_dtype == 0) {
+    if (p.silu) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, true, 64, 64, 2, 2>(a, stream);
+      return launch_cfg<AbType::F32, CType::F32, true, 64, 64, 2, 2>(a, stream);
+    }
+    if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, false, 64, 64, 2, 2>(a, stream);
+    return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2>(a, stream);
+  }
+  // fp8 operands
+  if (p.silu) {
+    if (p.c_dtype == 2) return launch_cfg<AbType::FP8, CType::FP8, true, 128, 256, 2, 2>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, true, 128, 256, 2, 2>(a, stream);
+    return launch_cfg<AbType::FP8, CType::F32, true, 128, 256, 2, 2>(a, stream);
+  }
+  if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, false, 128, 128, 2, 2>(a, stream);
+  return launch_cfg<AbType::FP8, CType::F32, false, 128, 128, 2, 2>(a, stream);
+}
+
+}  // namespace moe

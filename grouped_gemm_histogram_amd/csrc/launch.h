@@ -1,0 +1,43 @@
+// launch.h -- internal launchers behind the C ABI (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, long long valid_rows,
+                             int renorm, int* ids, float* weights, hipStream_t stream);
+
+size_t build_offsets_workspace_bytes(long long R, int E);
+hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int* sorted_rows,
+                                int* row_pos, void* workspace, hipStream_t stream);
+
+hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
+                               const int* offsets, int E, int R, void* xp, hipStream_t stream);
+hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
+                                const int* offsets, int E, int R, void* xq, float* xs,
+                                hipStream_t stream);
+
+struct GemmLaunch {
+  const void* A;
+  const float* a_scales;
+  const void* B;
+  const float* b_scales;
+  int ab_dtype;  // moe_dtype_t
+  const int* offsets;
+  int E;
+  long long M_rows, N, K;
+  bool silu;
+  void* C;
+  int c_dtype;   // moe_dtype_t
+  float* c_scales;
+};
+hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const float* weights,
+                          const int* offsets, int E, int T, int H, int k, void* out, bool out_bf16,
+                          hipStream_t stream);
+
+}  // namespace moe

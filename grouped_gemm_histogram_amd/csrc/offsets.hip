@@ -1,0 +1,132 @@
+// offsets.hip -- per-expert histogram (sentinel bin counted out), exclusive scan,
+// and the stable counting-sort permutation.
+//
+// The transformers PR #45621 write-up, section 2: sentinel rows must not be
+// computed (no clamping onto the last expert); they are left out of the
+// histogram or sorted as the largest key, and offsets[-1] is the number of
+// valid rows.  Here the sentinel is bin E of an (E+1)-bin histogram; offsets
+// stops before it, and the permutation places bin E last.
+//
+// Three small launches, no atomics on global memory, deterministic:
+//   1. hist:    one workgroup per chunk of rows, LDS histogram over E+1 bins.
+//   2. scan:    one workgroup; per-bin exclusive scan over chunks, then the
+//               exclusive scan over bins -> offsets and each chunk's base.
+//   3. scatter: one wave per chunk walks its rows in order, 64 at a time; a
+//               row's rank among equal ids in the same 64 comes from ballots
+//               over the id bits (lanes with equal ids), so ties keep flat
+//               order without any atomic.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;      // rows per chunk
+constexpr int kMaxBins = 1025;    // E + 1 with E <= 1024
+
+__device__ __forceinline__ int bin_of(int id, int E) { return (id >= 0 && id < E) ? id : E; }
+
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, int R, int E,
+                                                   int* __restrict__ chunk_hist) {
+  __shared__ int h[kMaxBins];
+  const int nb = E + 1;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * kChunk;
+  const int r1 = min(R, r0 + kChunk);
+  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) atomicAdd(&h[bin_of(ids[r], E)], 1);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) chunk_hist[(size_t)blockIdx.x * nb + i] = h[i];
+}
+
+// One workgroup of 1024 threads.  chunk_hist [nchunks][E+1] becomes, in place,
+// the first permuted position of each (chunk, bin).
+__global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist, int nchunks,
+                                                    int E, int* __restrict__ offsets) {
+  __shared__ int tot[2][kMaxBins + 1];
+  const int nb = E + 1;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk_hist[(size_t)c * nb + b];
+      chunk_hist[(size_t)c * nb + b] = run;
+      run += v;
+    }
+    tot[0][b] = run;
+  }
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the nb bin totals.
+  int src = 0;
+  for (int d = 1; d < nb; d <<= 1) {
+    for (int b = threadIdx.x; b < nb; b += blockDim.x)
+      tot[src ^ 1][b] = tot[src][b] + (b >= d ? tot[src][b - d] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const int base = (b == 0) ? 0 : tot[src][b - 1];   // exclusive
+    offsets[b] = base;                                  // offsets[E] = valid rows
+    for (int c = 0; c < nchunks; ++c) chunk_hist[(size_t)c * nb + b] += base;
+  }
+}
+
+// One wave per chunk.
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int R, int E,
+                                                     int id_bits,
+                                                     const int* __restrict__ chunk_base,
+                                                     int* __restrict__ sorted_rows,
+                                                     int* __restrict__ row_pos) {
+  __shared__ int cursor[kMaxBins];
+  const int nb = E + 1;
+  const int lane = lane_id();
+  for (int i = lane; i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i];
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int r0 = blockIdx.x * kChunk;
+  const int r1 = min(R, r0 + kChunk);
+  for (int base = r0; base < r1; base += kWave) {
+    const int r = base + lane;
+    const bool active = r < r1;
+    const int key = active ? bin_of(ids[r], E) : 0;
+    uint64_t same = __ballot(active);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int cnt = __popcll(same);
+    int pos = 0;
+    if (active) pos = cursor[key] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (active && rank == cnt - 1) cursor[key] = pos + 1;
+    __builtin_amdgcn_wave_barrier();
+    if (active) {
+      sorted_rows[pos] = r;
+      row_pos[r] = pos;
+    }
+  }
+}
+
+size_t build_offsets_workspace_bytes(long long R, int E) {
+  const long long nchunks = (R + kChunk - 1) / kChunk;
+  return (size_t)(nchunks > 0 ? nchunks : 1) * (size_t)(E + 1) * sizeof(int);
+}
+
+hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int* sorted_rows,
+                                int* row_pos, void* workspace, hipStream_t stream) {
+  const int nchunks = (R + kChunk - 1) / kChunk;
+  int* chunk_hist = static_cast<int*>(workspace);
+  int id_bits = 1;
+  while ((1 << id_bits) <= E) ++id_bits;   // bins 0..E need id_bits bits
+  if (nchunks > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, chunk_hist);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E,
+                     offsets);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, stream, ids, R, E, id_bits,
+                       chunk_hist, sorted_rows, row_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

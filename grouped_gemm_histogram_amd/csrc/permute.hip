@@ -1,0 +1,105 @@
+// permute.hip -- token rows into expert-contiguous order (the scatter step of the
+// LlamaFactory PR #10481 write-up, section 1), optionally quantising each row
+// to OCP e4m3 per 128 channels (the per-token activation cast the
+// transformers PR #45621 write-up, section 1, loads as fp8_act_quant /
+// per_token_cast_to_fp8).
+//
+// One wave per permuted row; 16-byte loads and stores, so each row moves as
+// coalesced 1 KiB wave transactions.  Positions at or past offsets[E] (the
+// sentinel tail) are skipped without touching memory.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+// x [T, n16 x 16 B] -> xp [R, n16 x 16 B]
+__global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restrict__ x, int T,
+                                                           int n16, int k, const int* __restrict__ sorted_rows,
+                                                           const int* __restrict__ offsets, int E,
+                                                           int R, uint4* __restrict__ xp) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (p >= R || p >= offsets[E]) return;
+  const int src = sorted_rows[p] / k;
+  if (src < 0 || src >= T) return;   // inconsistent permutation: leave the row unwritten
+  const uint4* s = x + (size_t)src * n16;
+  uint4* d = xp + (size_t)p * n16;
+  int c = lane;
+  for (; c + 3 * kWave < n16; c += 4 * kWave) {
+    const uint4 a0 = s[c], a1 = s[c + kWave], a2 = s[c + 2 * kWave], a3 = s[c + 3 * kWave];
+    d[c] = a0;
+    d[c + kWave] = a1;
+    d[c + 2 * kWave] = a2;
+    d[c + 3 * kWave] = a3;
+  }
+  for (; c < n16; c += kWave) d[c] = s[c];
+}
+
+// bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [R, H/128]; H % 128 == 0.
+// Each 16-lane group of the wave owns one 128-channel group per step.
+__global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restrict__ x, int T,
+                                                            int H, int k, const int* __restrict__ sorted_rows,
+                                                            const int* __restrict__ offsets, int E,
+                                                            int R, uint2* __restrict__ xq,
+                                                            float* __restrict__ xs) {
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (p >= R || p >= offsets[E]) return;
+  const int src = sorted_rows[p] / k;
+  if (src < 0 || src >= T) return;   // inconsistent permutation: leave the row unwritten
+  const int n8 = H / 8;                       // 8-channel units per row
+  const uint4* s = x + (size_t)src * n8;
+  uint2* d = xq + (size_t)p * n8;
+  float* sc = xs + (size_t)p * (H / 128);
+  for (int base = 0; base < n8; base += kWave) {
+    const int u = base + lane;
+    const bool active = u < n8;               // whole 16-lane groups, as H % 128 == 0
+    float v[8];
+    float amax = 0.0f;
+    if (active) {
+      const uint4 raw = s[u];
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    if (active) {
+      const float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+      uint32_t lo = 0, hi = 0;
+      lo = cvt_e4m3x2(clamp448(v[0] / scale), clamp448(v[1] / scale)) |
+           (cvt_e4m3x2(clamp448(v[2] / scale), clamp448(v[3] / scale)) << 16);
+      hi = cvt_e4m3x2(clamp448(v[4] / scale), clamp448(v[5] / scale)) |
+           (cvt_e4m3x2(clamp448(v[6] / scale), clamp448(v[7] / scale)) << 16);
+      d[u] = make_uint2(lo, hi);
+      if ((lane & 15) == 0) sc[u / 16] = scale;
+    }
+  }
+}
+
+hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
+                               const int* offsets, int E, int R, void* xp, hipStream_t stream) {
+  if (R > 0)
+    hipLaunchKernelGGL(permute_copy_kernel, dim3((R + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const uint4*>(x), T, row_bytes / 16, k, sorted_rows, offsets, E, R,
+                       static_cast<uint4*>(xp));
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
+                                const int* offsets, int E, int R, void* xq, float* xs,
+                                hipStream_t stream) {
+  if (R > 0)
+    hipLaunchKernelGGL(permute_quant_kernel, dim3((R + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const uint4*>(x), T, H, k, sorted_rows, offsets, E, R,
+                       static_cast<uint2*>(xq), xs);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,210 @@
+"""Torch-tensor wrappers over the C ABI: argument marshalling only.
+
+Every function checks devices, dtypes, shapes and contiguity, allocates its
+outputs with torch (device memory and the current stream are torch's), and
+calls the HIP library; a non-OK status raises RuntimeError with the
+library's message.  There is no fallback: without the built library on a
+GPU, ``load()`` raises ImportError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MoeAux, load
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16,
+       torch.float8_e4m3fn: _lib.MOE_FP8_E4M3}
+_EPI = {"none": _lib.MOE_EPI_NONE, "silu_mul": _lib.MOE_EPI_SILU_MUL}
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int) -> None:
+    if status != _lib.MOE_OK:
+        lib = load()
+        raise RuntimeError(f"{lib.status_string(status).decode()}: {lib.last_error().decode()}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def route_topk(logits: torch.Tensor, k: int, num_valid_rows: int = -1, renormalize: bool = True):
+    """logits f32 [T, E] -> (topk_ids int32 [T, k], topk_weights f32 [T, k])."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check(load().route_topk(_p(logits), T, E, k, num_valid_rows, int(bool(renormalize)),
+                             _p(ids), _p(w), _stream(logits)))
+    return ids, w
+
+
+def build_offsets(topk_ids: torch.Tensor, E: int):
+    """flat ids int32 [R] -> (offsets int32 [E+1], sorted_rows int32 [R], row_pos int32 [R])."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    ids = topk_ids.reshape(-1)
+    R = ids.numel()
+    dev = ids.device
+    lib = load()
+    ws = torch.empty(max(1, lib.build_offsets_workspace(R, E)), dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_rows = torch.empty(R, dtype=torch.int32, device=dev)
+    row_pos = torch.empty(R, dtype=torch.int32, device=dev)
+    _check(lib.build_offsets(_p(ids), R, E, _p(offsets), _p(sorted_rows), _p(row_pos), _p(ws),
+                             ws.numel(), _stream(ids)))
+    return offsets, sorted_rows, row_pos
+
+
+def permute(x: torch.Tensor, sorted_rows: torch.Tensor, offsets: torch.Tensor, k: int,
+            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+            out_scales: Optional[torch.Tensor] = None):
+    """x [T, H] -> x_perm [R, H] (rows >= offsets[E] untouched); fp8 also returns scales [R, H/128]."""
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    T, H = x.shape
+    R = sorted_rows.numel()
+    E = offsets.numel() - 1
+    out_dtype = out_dtype or x.dtype
+    _need(sorted_rows, "sorted_rows", torch.int32, device=x.device)
+    _need(offsets, "offsets", torch.int32, device=x.device)
+    if out is None:
+        out = torch.empty(R, H, dtype=out_dtype, device=x.device)
+    _need(out, "out", out_dtype, (R, H), x.device)
+    fp8 = out_dtype == torch.float8_e4m3fn
+    if fp8 and out_scales is None:
+        out_scales = torch.empty(R, H // 128, dtype=torch.float32, device=x.device)
+    _check(load().permute(_p(x), _DT[x.dtype], T, H, k, _p(sorted_rows), _p(offsets), E, R,
+                          _p(out), _DT[out_dtype], _p(out_scales) if fp8 else None, _stream(x)))
+    return (out, out_scales) if fp8 else out
+
+
+def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilogue: str = "none",
+                 a_scales: Optional[torch.Tensor] = None, b_scales: Optional[torch.Tensor] = None,
+                 out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                 out_scales: Optional[torch.Tensor] = None):
+    """a [M, K] x b [E, N, K] over segments of offsets -> c [M, N or N/2] (+ scales for fp8 out)."""
+    _need(a, "a", tuple(_DT))
+    M, K = a.shape
+    E, N, K2 = b.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: a has {K}, b has {K2}")
+    _need(b, "b", a.dtype, device=a.device)
+    _need(offsets, "offsets", torch.int32, (E + 1,), a.device)
+    fp8 = a.dtype == torch.float8_e4m3fn
+    if fp8:
+        _need(a_scales, "a_scales", torch.float32, (M, K // 128), a.device)
+        _need(b_scales, "b_scales", torch.float32, (E, N // 128, K // 128), a.device)
+    n_out = N // 2 if epilogue == "silu_mul" else N
+    out_dtype = out_dtype or (torch.bfloat16 if fp8 else a.dtype)
+    if out is None:
+        out = torch.empty(M, n_out, dtype=out_dtype, device=a.device)
+    _need(out, "out", out_dtype, (M, n_out), a.device)
+    fp8_out = out_dtype == torch.float8_e4m3fn
+    if fp8_out and out_scales is None:
+        out_scales = torch.empty(M, n_out // 128, dtype=torch.float32, device=a.device)
+    _check(load().grouped_gemm(_p(a), _p(a_scales) if fp8 else None, _p(b),
+                               _p(b_scales) if fp8 else None, _DT[a.dtype], _p(offsets), E, M, N, K,
+                               _EPI[epilogue], _p(out), _DT[out_dtype],
+                               _p(out_scales) if fp8_out else None, _stream(a)))
+    return (out, out_scales) if fp8_out else out
+
+
+def unpermute_combine(y: torch.Tensor, row_pos: torch.Tensor, topk_weights: torch.Tensor,
+                      offsets: torch.Tensor, k: int, out_dtype: Optional[torch.dtype] = None,
+                      out: Optional[torch.Tensor] = None):
+    """y [R, H] -> out [T, H] = weighted sum of each token's valid rows."""
+    _need(y, "y", (torch.float32, torch.bfloat16))
+    R, H = y.shape
+    T = R // k
+    E = offsets.numel() - 1
+    _need(row_pos, "row_pos", torch.int32, device=y.device)
+    _need(topk_weights, "topk_weights", torch.float32, device=y.device)
+    _need(offsets, "offsets", torch.int32, device=y.device)
+    out_dtype = out_dtype or y.dtype
+    if out is None:
+        out = torch.empty(T, H, dtype=out_dtype, device=y.device)
+    _need(out, "out", out_dtype, (T, H), y.device)
+    _check(load().unpermute_combine(_p(y), _DT[y.dtype], _p(row_pos), _p(topk_weights), _p(offsets),
+                                    E, T, H, k, _p(out), _DT[out_dtype], _stream(y)))
+    return out
+
+
+@dataclass
+class ForwardAux:
+    topk_ids: torch.Tensor
+    topk_weights: torch.Tensor
+    offsets: torch.Tensor
+    sorted_rows: torch.Tensor
+    row_pos: torch.Tensor
+
+
+def forward_workspace_bytes(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype) -> int:
+    return load().forward_workspace(T, H, I, E, k, _DT[w_dtype])
+
+
+def forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, k: int,
+            num_valid_rows: int = -1, renormalize: bool = True,
+            w13_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None,
+            out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
+    """The whole layer: x [T, H], logits f32 [T, E], w13 [E, 2I, H], w2 [E, H, I] -> out [T, H]."""
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    dev = x.device
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    _need(w13, "w13", tuple(_DT), (E, 2 * I, H), dev)
+    _need(w2, "w2", w13.dtype, (E, H, I), dev)
+    fp8 = w13.dtype == torch.float8_e4m3fn
+    if fp8:
+        _need(w13_scale, "w13_scale", torch.float32, (E, 2 * I // 128, H // 128), dev)
+        _need(w2_scale, "w2_scale", torch.float32, (E, H // 128, I // 128), dev)
+    out_dtype = out_dtype or (torch.float32 if w13.dtype == torch.float32 else torch.bfloat16)
+    if out is None:
+        out = torch.empty(T, H, dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (T, H), dev)
+    lib = load()
+    need = lib.forward_workspace(T, H, I, E, k, _DT[w13.dtype])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    aux_t = None
+    aux_c = None
+    if return_aux:
+        R = T * k
+        aux_t = ForwardAux(torch.empty(T, k, dtype=torch.int32, device=dev),
+                           torch.empty(T, k, dtype=torch.float32, device=dev),
+                           torch.empty(E + 1, dtype=torch.int32, device=dev),
+                           torch.empty(R, dtype=torch.int32, device=dev),
+                           torch.empty(R, dtype=torch.int32, device=dev))
+        aux_c = MoeAux(aux_t.topk_ids.data_ptr(), aux_t.topk_weights.data_ptr(),
+                       aux_t.offsets.data_ptr(), aux_t.sorted_rows.data_ptr(),
+                       aux_t.row_pos.data_ptr())
+    _check(lib.forward(_p(x), _DT[x.dtype], _p(logits), _p(w13), _p(w13_scale) if fp8 else None,
+                       _p(w2), _p(w2_scale) if fp8 else None, _DT[w13.dtype], T, H, I, E, k,
+                       num_valid_rows, int(bool(renormalize)), _p(out), _DT[out_dtype],
+                       ctypes.byref(aux_c) if aux_c is not None else None, _p(workspace),
+                       workspace.numel(), _stream(x)))
+    return (out, aux_t) if return_aux else out

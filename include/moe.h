@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of the MoE expert layer's grouped-GEMM path for MI355X (gfx950).
+ *
+ * The path: top-k routing -> per-expert histogram with sentinel rows counted
+ * out -> exclusive-scan offsets -> stable permutation into expert-contiguous
+ * order -> grouped GEMM gate/up with a fused SiLU(gate)*up -> grouped GEMM
+ * down -> routing-weight-scaled combine back to token order.
+ *
+ * Sources (the three web write-ups the method is described in):
+ *   [T45621]  "Hugging Face Transformers: MoE 및 FP8 커널 최적화를 통한 성능 향상"
+ *             (transformers PR #45621 analysis); section 1 (kernel loading),
+ *             section 2 (sentinel-token handling), section 3 (fp8 NaN fix).
+ *   [LF10481] "LlamaFactory의 Triton 기반 Fused MoE 커널 도입"
+ *             (LlamaFactory PR #10481 analysis); section 1 (fused MoE pipeline).
+ *   [MoEs]    "트랜스포머에서 전문가 혼합 (MoEs)"; sections on MoE basics,
+ *             WeightConverter, expert backends and expert parallelism.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *    densely packed (no padding between rows), 16-byte aligned.
+ *  - Flat routed row r = t*k + j (token t, slot j).  R = T*k.
+ *  - Expert id E is the sentinel: a row that is not computed (unrouted or
+ *    padding).  Ids outside [0, E] are treated as sentinel as well.
+ *  - offsets is int32[E+1]: offsets[0] = 0, offsets[e+1] - offsets[e] = rows
+ *    routed to expert e, offsets[E] = V = number of valid (non-sentinel) rows.
+ *    Permuted positions [offsets[e], offsets[e+1]) belong to expert e;
+ *    positions [V, R) are sentinel.
+ *  - Packed weights are expert-major (the stacked layout of [MoEs],
+ *    WeightConverter / MergeModulelist): gate/up W13 [E, 2I, H] with rows
+ *    [0, I) = gate and [I, 2I) = up; down W2 [E, H, I].  Both are [E, N, K]
+ *    with K contiguous.
+ *  - fp8 is OCP E4M3 ("e4m3fn", max 448).  fp8 weights carry one fp32 scale
+ *    per 128x128 block ([E, N/128, K/128]); fp8 activations carry one fp32
+ *    scale per row and 128 consecutive channels ([rows, K/128]).  A value is
+ *    code * scale.  Activation scales are amax/448 (1 for an all-zero group),
+ *    codes are round-to-nearest-even of value/scale, saturating.
+ *  - Every call validates its arguments on the host first and returns
+ *    MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE without
+ *    launching anything when they fail.  Otherwise it enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL = the default stream) and returns without
+ *    synchronising; a launch failure returns MOE_ERR_LAUNCH.  No call
+ *    allocates or frees memory or keeps a pointer after it returns.  No C++
+ *    exception crosses this boundary.  moe_last_error() gives a thread-local
+ *    message for the last non-OK status.
+ *  - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 16), R = T*k < 2^31.
+ *  - Results are deterministic: repeated calls on the same inputs give
+ *    bitwise-identical outputs (no floating-point atomics, no split-K).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_LAUNCH = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+
+typedef enum { MOE_EPI_NONE = 0, MOE_EPI_SILU_MUL = 1 } moe_epilogue_t;
+
+/*
+ * moe_route_topk -- the router's choice of a small subset of experts per
+ * token ([MoEs], MoE basics).
+ *
+ *   logits        f32 [T, E], finite values.
+ *   topk_ids      out int32 [T, k]: slot j holds the expert with the j-th
+ *                 largest logit; equal logits go to the lower expert id.
+ *   topk_weights  out f32 [T, k]: renormalize = 1: softmax over the k
+ *                 selected logits; renormalize = 0: softmax over all E logits
+ *                 read at the selected experts.
+ *   num_valid_rows  < 0: all R = T*k flat rows are valid; otherwise flat rows
+ *                 r >= num_valid_rows are written as sentinel (id = E,
+ *                 weight = 0).
+ */
+moe_status_t moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                            int64_t num_valid_rows, int32_t renormalize,
+                            int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Bytes of device workspace moe_build_offsets needs for R rows and E experts. */
+size_t moe_build_offsets_workspace(int64_t R, int32_t E);
+
+/*
+ * moe_build_offsets -- per-expert histogram with the sentinel bin left out,
+ * its exclusive scan, and the stable permutation ([T45621] section 2:
+ * sentinel rows are excluded from the histogram, or sorted as the largest key
+ * so that they fall to the end; offsets[-1] is the valid-row count; [MoEs]
+ * expert backends: grouped_mm sorts tokens by expert id).
+ *
+ *   topk_ids     int32 [R], values in [0, E]; E (or anything outside
+ *                [0, E]) = sentinel.
+ *   offsets      out int32 [E+1] (see conventions).
+ *   sorted_rows  out int32 [R]: flat row at each permuted position; rows of
+ *                one expert in ascending flat order, sentinel rows last (also
+ *                ascending).
+ *   row_pos      out int32 [R]: inverse of sorted_rows.
+ *   workspace    device scratch of >= moe_build_offsets_workspace(R, E)
+ *                bytes (else MOE_ERR_WORKSPACE); contents need no
+ *                initialisation and are garbage afterwards.
+ */
+moe_status_t moe_build_offsets(const int32_t* topk_ids, int64_t R, int32_t E,
+                               int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute -- moves token rows into expert-contiguous order (the
+ * scatter step of [LF10481] section 1): x_perm[p] = x[sorted_rows[p] / k]
+ * for p < offsets[E].  Rows p >= offsets[E] of x_perm are not written.
+ *
+ *   x            [T, H] of x_dtype (MOE_F32 or MOE_BF16).
+ *   perm_dtype   == x_dtype: exact copy.  MOE_FP8_E4M3 (x_dtype MOE_BF16,
+ *                H % 128 == 0): each row is quantised per 128 channels
+ *                (the per-token activation cast that [T45621] section 1
+ *                loads as fp8_act_quant / per_token_cast_to_fp8) into
+ *                x_perm codes [R, H] and x_perm_scales f32 [R, H/128].
+ *   R            rows of x_perm (>= offsets[E]); T*k for the layer.
+ */
+moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t H, int32_t k,
+                         const int32_t* sorted_rows, const int32_t* offsets, int32_t E,
+                         int64_t R, void* x_perm, moe_dtype_t perm_dtype,
+                         float* x_perm_scales, void* stream);
+
+/*
+ * moe_grouped_gemm -- one GEMM per expert over its row segment, same N and K
+ * for every group (the group_gemm_same_nk step of [LF10481] section 1;
+ * [MoEs] expert backends, grouped_mm):
+ *
+ *   for p in [offsets[e], offsets[e+1]):  acc[p, n] = sum_k A[p, k] * B[e, n, k]
+ *
+ *   A         [M_rows, K] of ab_dtype; a_scales f32 [M_rows, K/128] for fp8.
+ *   B         [E, N, K] of ab_dtype;   b_scales f32 [E, N/128, K/128] for fp8.
+ *   ab_dtype  MOE_F32, MOE_BF16 or MOE_FP8_E4M3 (K % 128 == 0 for fp8).
+ *   offsets   device int32 [E+1]; read on the device (no host sync).
+ *   epi       MOE_EPI_NONE: C = acc, N_out = N.
+ *             MOE_EPI_SILU_MUL: N even, B rows [0, N/2) are gate and
+ *             [N/2, N) up; C = silu(gate) * up, N_out = N/2 (the
+ *             SiLU(fc1_1) * fc1_2 step of [LF10481] section 1).
+ *   C         [M_rows, N_out] of c_dtype: MOE_F32, MOE_BF16, or MOE_FP8_E4M3
+ *             (ab_dtype fp8 and N_out % 128 == 0: rows quantised per 128
+ *             channels from the fp32 result, scales in c_scales
+ *             f32 [M_rows, N_out/128]).
+ *
+ * Only rows below offsets[E] are computed: no tile is launched past the last
+ * valid row.  Rows [offsets[E], M_rows) of C are written as exact zeros
+ * (their fp8 scales as 1.0) -- never left uninitialised ([T45621] section 3
+ * traces a NaN to sentinel outputs that a kernel left unwritten).
+ * Accumulation is fp32; C is rounded once (RNE).
+ */
+moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* B,
+                              const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
+                              int32_t E, int64_t M_rows, int64_t N, int64_t K,
+                              moe_epilogue_t epi, void* C, moe_dtype_t c_dtype, float* c_scales,
+                              void* stream);
+
+/*
+ * moe_unpermute_combine -- back to token order, scaled by the routing
+ * weights (the gather step of [LF10481] section 1):
+ *
+ *   out[t] = sum over j = 0..k-1 (ascending) with row_pos[t*k+j] < offsets[E]
+ *            of topk_weights[t*k+j] * y[row_pos[t*k+j]]
+ *
+ * accumulated in fp32 and rounded once to out_dtype.  Tokens with no valid
+ * row get exact zeros.  Sentinel rows of y are never read.
+ *
+ *   y            [R, H] of y_dtype (MOE_F32 or MOE_BF16).
+ *   out          [T, H] of out_dtype (MOE_F32 or MOE_BF16).
+ */
+moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int32_t* row_pos,
+                                   const float* topk_weights, const int32_t* offsets, int32_t E,
+                                   int64_t T, int64_t H, int32_t k, void* out,
+                                   moe_dtype_t out_dtype, void* stream);
+
+/* Optional caller-owned storage for the routing intermediates of moe_forward.
+ * Each non-NULL pointer is used instead of workspace storage, so the caller
+ * can read the values after the stream completes. */
+typedef struct {
+  int32_t* topk_ids;      /* [T*k]  */
+  float* topk_weights;    /* [T*k]  */
+  int32_t* offsets;       /* [E+1]  */
+  int32_t* sorted_rows;   /* [T*k]  */
+  int32_t* row_pos;       /* [T*k]  */
+} moe_aux_t;
+
+/* Bytes of device workspace moe_forward needs (routing arrays, permuted
+ * activations, h, per-row expert outputs). */
+size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                             moe_dtype_t w_dtype);
+
+/*
+ * moe_forward -- the whole layer on one stream: route, offsets, permute,
+ * grouped GEMM gate/up + SiLU*up, grouped GEMM down, combine ([LF10481]
+ * section 1 pipeline; [T45621] section 2 sentinel exclusion).
+ *
+ *   x            [T, H]: MOE_F32 when w_dtype is MOE_F32, else MOE_BF16.
+ *   router_logits f32 [T, E].
+ *   w13, w2      packed weights of w_dtype (MOE_F32, MOE_BF16 or
+ *                MOE_FP8_E4M3); w13_scales [E, 2I/128, H/128] and
+ *                w2_scales [E, H/128, I/128] for fp8 (H, I % 128 == 0).
+ *   num_valid_rows, renormalize: as for moe_route_topk.
+ *   out          [T, H] of out_dtype (MOE_F32 for f32 weights, else MOE_BF16).
+ *   aux          nullable; see moe_aux_t.
+ *   workspace    >= moe_forward_workspace(...) bytes; no initialisation needed.
+ *
+ * Intermediates: f32 weights keep f32 throughout; bf16 weights round h and
+ * the expert outputs to bf16; fp8 weights quantise the permuted activations
+ * and h per row and 128 channels, and keep expert outputs in bf16.
+ */
+moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router_logits,
+                         const void* w13, const float* w13_scales, const void* w2,
+                         const float* w2_scales, moe_dtype_t w_dtype, int64_t T, int64_t H,
+                         int64_t I, int32_t E, int32_t k, int64_t num_valid_rows,
+                         int32_t renormalize, void* out, moe_dtype_t out_dtype, moe_aux_t* aux,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Short name of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Thread-local message describing the last non-OK status returned on this
+ * thread ("" if none). */
+const char* moe_last_error(void);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

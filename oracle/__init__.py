@@ -37,4 +37,4 @@ textbook SwiGLU via torch, torch's e4m3 cast, the valid-row counts the
 transformers write-up prints, invariants).  Nothing here is "parity unpinned".
 """
 
-from . import e4m3, routing, layer, brute  # noqa: F401
+from . import e4m3, routing, layer, gemm, brute  # noqa: F401

@@ -25,8 +25,7 @@ import numpy as np
 MAX = 448.0
 
 
-def decode(codes) -> np.ndarray:
-    """uint8 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+def _decode_formula(codes) -> np.ndarray:
     c = np.asarray(codes).astype(np.int64)
     sign = np.where(c >> 7, -1.0, 1.0)
     e = (c >> 3) & 15
@@ -35,6 +34,15 @@ def decode(codes) -> np.ndarray:
     nrm = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
     val = np.where(e == 0, sub, nrm) * sign
     return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+# The value of every code, from the formula above; decoding is a table lookup.
+_TABLE = _decode_formula(np.arange(256))
+
+
+def decode(codes) -> np.ndarray:
+    """uint8 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    return _TABLE[np.asarray(codes).astype(np.uint8)]
 
 
 # Non-negative finite codes 0x00..0x7E in order; their values increase with the code.

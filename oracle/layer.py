@@ -215,6 +215,39 @@ def token_output(x_t, ids_t, w_t, W: ExpertWeights, weight_cache: dict | None = 
     return out
 
 
+def sampled_outputs(x_rows, ids_rows, w_rows, W: ExpertWeights) -> np.ndarray:
+    """Outputs of a few tokens (rows of x with their routed ids and weights).
+
+    The same definition as ``token_output``, organised by expert so that each
+    expert's weights are converted once: for every expert used by the sample,
+    h and the expert output are computed for the sample rows routed to it;
+    each token then sums its slots in ascending order.
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float32)
+    S, H = x_rows.shape
+    k = np.asarray(ids_rows).shape[1]
+    E, I = W.E, W.I
+    if W.fp8:
+        q, s = quant128(x_rows)
+        xv = dequant128(q, s)
+    else:
+        xv = x_rows.astype(np.float64)
+    y = np.zeros((S, k, H), dtype=np.float64)
+    ids_rows = np.asarray(ids_rows)
+    for e in sorted(set(int(v) for v in ids_rows.reshape(-1) if 0 <= v < E)):
+        sel = np.argwhere(ids_rows == e)              # (sample, slot) pairs routed to e
+        h = expert_h(xv[sel[:, 0]], W.gate_up(e), I)
+        if W.fp8:
+            hq, hs = quant128(h.astype(np.float32))
+            h = dequant128(hq, hs)
+        y[sel[:, 0], sel[:, 1]] = h @ W.down(e).T
+    out = np.zeros((S, H), dtype=np.float64)
+    for j in range(k):
+        valid = (ids_rows[:, j] >= 0) & (ids_rows[:, j] < E)
+        out += np.where(valid[:, None], np.asarray(w_rows, np.float64)[:, j:j + 1] * y[:, j], 0.0)
+    return out
+
+
 def layer_forward_dense_inputs(inputs) -> dict:
     """Convenience: run ``forward`` on a workloads.LayerInputs (tensors on the CPU)."""
     import torch  # plain tensor-to-array conversion only

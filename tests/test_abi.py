@@ -1,0 +1,77 @@
+"""The C-ABI library: builds, loads, exports what include/moe.h declares, validates on the host.
+
+No call here reaches a GPU: every call fails host-side validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from grouped_gemm_histogram_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from grouped_gemm_histogram_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_route_topk", "moe_build_offsets", "moe_permute", "moe_grouped_gemm",
+              "moe_unpermute_combine", "moe_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    so = ctypes.CDLL(lib.path)
+    for n in declared_functions():
+        assert hasattr(so, n), n
+    from grouped_gemm_histogram_amd._lib import SIGNATURES
+    assert set(SIGNATURES) == set(declared_functions())
+
+
+def test_version_and_strings(lib):
+    assert lib.abi_version() == 1
+    assert lib.status_string(0) == b"MOE_OK"
+    assert lib.status_string(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_host_validation(lib):
+    INVALID, UNSUP, WS = 1, 2, 3
+    assert lib.route_topk(None, 4, 0, 1, -1, 1, None, None, None) == INVALID
+    assert b"E=0" in lib.last_error()
+    assert lib.route_topk(None, 4, 8, 9, -1, 1, None, None, None) == INVALID     # k > E
+    assert lib.route_topk(None, 4, 64, 17, -1, 1, None, None, None) == INVALID   # k > 16
+    assert lib.route_topk(None, 4, 2000, 2, -1, 1, None, None, None) == INVALID  # E > 1024
+    assert lib.route_topk(None, 4, 8, 2, -1, 1, None, None, None) == INVALID     # null pointers
+    assert lib.route_topk(None, 0, 8, 2, -1, 1, None, None, None) == 0           # empty: no-op
+    assert lib.build_offsets_workspace(65536, 256) >= 64 * 257 * 4
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.build_offsets(fake, 100, 8, fake, fake, fake, fake, 1, None) == WS
+    # grouped GEMM shape rules
+    assert lib.grouped_gemm(fake, None, fake, None, 1, fake, 8, 64, 7, 64, 1, fake, 1, None, None) == INVALID  # odd N
+    assert lib.grouped_gemm(fake, None, fake, None, 1, fake, 8, 64, 64, 60, 0, fake, 1, None, None) == INVALID  # K*2 % 16
+    assert lib.grouped_gemm(fake, None, fake, None, 2, fake, 8, 64, 256, 256, 0, fake, 1, None, None) == INVALID  # fp8 w/o scales
+    assert lib.grouped_gemm(fake, None, fake, None, 1, fake, 8, 64, 256, 256, 0, fake, 2, None, None) == UNSUP  # bf16 -> fp8
+    assert lib.grouped_gemm(ctypes.c_void_p(0x1001), None, fake, None, 1, fake, 8, 64, 256, 256, 0,
+                            fake, 1, None, None) == INVALID                                   # misaligned
+    assert lib.permute(fake, 1, 4, 100, 2, fake, fake, 8, 8, fake, 2, None, None) == INVALID   # fp8 H%128
+    assert lib.permute(fake, 2, 4, 128, 2, fake, fake, 8, 8, fake, 1, None, None) == INVALID   # x fp8
+    assert lib.unpermute_combine(fake, 1, fake, fake, fake, 8, 4, 12, 2, fake, 1, None) == INVALID  # H*2 % 16
+    assert lib.forward_workspace(4096, 2880, 2880, 32, 4, 1) > 3 * 16384 * 2880 * 2
+    assert lib.forward(fake, 1, fake, fake, None, fake, None, 1, 16, 64, 64, 4, 2, -1, 1, fake, 1,
+                       None, fake, 10, None) == WS
+    assert lib.forward(fake, 0, fake, fake, None, fake, None, 1, 16, 64, 64, 4, 2, -1, 1, fake, 1,
+                       None, fake, 1 << 30, None) == INVALID                                  # x dtype

@@ -1,0 +1,346 @@
+"""Per-kernel parity of the HIP path against the oracle, through the C ABI.
+
+Bar: routing ids, offsets, permutations, permuted rows and fp8 activation
+codes/scales bit-exact; routing weights within 1e-5 relative; GEMM / combine
+outputs within the row-normalised tolerance of their dtype (bf16 1e-2, fp8
+2e-2, f32 1e-4), bit-exact on exact-arithmetic inputs; sentinel rows exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, np32, npu8, row_rel_err, say
+from oracle import e4m3, gemm as ogemm, layer as olayer, routing as orouting
+from workloads import quantize_weight_blocks
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def ops():
+    import grouped_gemm_histogram_amd as g
+    g.load()
+    return g
+
+
+# ------------------------------------------------------------------------------------ routing
+
+ROUTE_CASES = [(1, 1, 1), (37, 8, 2), (500, 32, 4), (300, 64, 8), (257, 65, 3), (256, 128, 8),
+               (129, 256, 8), (64, 1000, 16), (33, 1024, 16), (4096, 32, 4), (8192, 256, 8)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+@pytest.mark.parametrize("ties", [False, True])
+def test_route_topk(T, E, k, ties):
+    say(f"route T={T} E={E} k={k} ties={ties}")
+    rng = np.random.default_rng(T * 7 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        lg = (np.round(lg * 2) / 2).astype(np.float32)
+        lg[lg == 0] = np.where(rng.random(np.count_nonzero(lg == 0)) < 0.5, -0.0, 0.0)
+    g = ops()
+    lt = torch.from_numpy(lg).to(DEV)
+    for nv in (-1, (T * k) // 3, 0):
+        for renorm in (True, False):
+            ids, w = g.route_topk(lt, k, nv, renorm)
+            rid, rw = orouting.route_topk(lg, k, nv, renorm)
+            torch.cuda.synchronize()
+            assert np.array_equal(ids.cpu().numpy(), rid), (nv, renorm)
+            np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-5, atol=1e-7)
+
+
+# ------------------------------------------------------------------------------------ offsets
+
+OFFSET_CASES = [(1, 1), (100, 3), (1000, 8), (1025, 8), (4096, 129), (16384, 128), (65536, 256),
+                (70000, 1024), (5000, 1024), (3000, 1)]
+
+
+@pytest.mark.parametrize("R,E", OFFSET_CASES)
+def test_build_offsets(R, E):
+    say(f"offsets R={R} E={E}")
+    rng = np.random.default_rng(R + 3 * E)
+    ids = rng.integers(0, E + 1, R).astype(np.int32)
+    ids[rng.random(R) < 0.03] = -5
+    ids[rng.random(R) < 0.03] = E + 11
+    g = ops()
+    off, sr, rp = g.build_offsets(torch.from_numpy(ids).to(DEV), E)
+    roff, rsr, rrp = orouting.build_offsets(ids, E)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sr.cpu().numpy(), rsr)
+    assert np.array_equal(rp.cpu().numpy(), rrp)
+
+
+@pytest.mark.parametrize("pattern", ["one_expert", "all_sentinel", "one_hot", "last_expert"])
+def test_build_offsets_degenerate(pattern):
+    say(f"offsets degenerate {pattern}")
+    R, E = 5000, 64
+    if pattern == "one_expert":
+        ids = np.full(R, 17, np.int32)
+    elif pattern == "all_sentinel":
+        ids = np.full(R, E, np.int32)
+    elif pattern == "one_hot":
+        ids = np.arange(R, dtype=np.int32) % E
+    else:
+        ids = np.where(np.arange(R) % 3 == 0, E - 1, E).astype(np.int32)
+    g = ops()
+    off, sr, rp = g.build_offsets(torch.from_numpy(ids).to(DEV), E)
+    roff, rsr, rrp = orouting.build_offsets(ids, E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sr.cpu().numpy(), rsr)
+    assert np.array_equal(rp.cpu().numpy(), rrp)
+
+
+def test_build_offsets_empty():
+    g = ops()
+    off, sr, rp = g.build_offsets(torch.empty(0, dtype=torch.int32, device=DEV), 8)
+    assert off.cpu().tolist() == [0] * 9
+
+
+# ------------------------------------------------------------------------------------ permute
+
+def _routing(T, E, k, nv, seed):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = orouting.route_topk(lg, k, nv)
+    off, sr, rp = orouting.build_offsets(ids.reshape(-1), E)
+    return ids, w, off, sr, rp
+
+
+@pytest.mark.parametrize("dtype,H", [(torch.bfloat16, 2880), (torch.bfloat16, 8), (torch.float32, 132),
+                                     (torch.float32, 4), (torch.bfloat16, 7168)])
+def test_permute_copy(dtype, H):
+    say(f"permute copy {dtype} H={H}")
+    T, E, k = 300, 16, 3
+    ids, w, off, sr, rp = _routing(T, E, k, 700, 1)
+    R = T * k
+    x = torch.randn(T, H, generator=torch.Generator().manual_seed(2)).to(dtype)
+    g = ops()
+    out = torch.full((R, H), float("nan"), dtype=dtype, device=DEV)
+    g.permute(x.to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(off).to(DEV), k, out=out)
+    got = out.cpu()
+    ref = olayer.permute_rows(x.view(torch.int16).numpy() if dtype == torch.bfloat16
+                              else x.view(torch.int32).numpy(), sr, off, k)
+    V = int(off[-1])
+    bits = got.view(torch.int16 if dtype == torch.bfloat16 else torch.int32).numpy()
+    assert np.array_equal(bits[:V], ref)
+    assert torch.isnan(got[V:].float()).all()          # sentinel tail never written
+
+
+def _sweep_rows():
+    """bf16 rows whose 128-groups each hold 448*2^m plus sweep values * 2^m (scale = 2^m exactly)."""
+    # every non-negative bf16 value up to 448, both signs, and their 2^m multiples
+    bits = np.arange(0, 0x43E1, dtype=np.uint32)           # 0x43E0 is 448.0 in bf16
+    vals = (bits << 16).view(np.float32)
+    vals = vals[(vals <= 448.0) & ((vals == 0) | (vals >= 2.0 ** -100))]   # no fp32 denormals
+    vals = np.concatenate([vals, -vals])
+    groups = []
+    for m in (-3, 0, 5):
+        for i in range(0, len(vals), 127):
+            grp = np.zeros(128, np.float32)
+            chunk = vals[i:i + 127]
+            grp[0] = 448.0
+            grp[1:1 + len(chunk)] = chunk
+            groups.append(grp * np.float32(2.0 ** m))
+    flat = np.concatenate(groups)
+    pad = (-len(flat)) % 512
+    return np.concatenate([flat, np.zeros(pad, np.float32)]).reshape(-1, 512)
+
+
+@pytest.mark.parametrize("case", ["random", "sweep"])
+def test_permute_quant_fp8(case):
+    say(f"permute quant fp8 {case}")
+    if case == "sweep":
+        xf = _sweep_rows()
+        T, H = xf.shape
+        x = torch.from_numpy(xf).to(torch.bfloat16)
+        assert np.array_equal(x.float().numpy(), xf)          # all sweep values exact in bf16
+        k, E = 1, 1
+        ids = np.zeros((T, 1), np.int32)
+        off, sr, rp = orouting.build_offsets(ids.reshape(-1), E)
+    else:
+        T, H, E, k = 200, 7168, 32, 8
+        ids, w, off, sr, rp = _routing(T, E, k, 1500, 3)
+        x = (torch.randn(T, H, generator=torch.Generator().manual_seed(4)) *
+             torch.exp(torch.randn(T, 1, generator=torch.Generator().manual_seed(5)))).to(torch.bfloat16)
+        x[3, :128] = 0                                        # all-zero group: scale 1
+    R = T * k
+    g = ops()
+    q, s = g.permute(x.to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(off).to(DEV), k,
+                     out_dtype=torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    xq, xs = olayer.quant128(x.float().numpy())
+    V = int(off[-1])
+    rq = olayer.permute_rows(xq, sr, off, k)
+    rs = olayer.permute_rows(xs, sr, off, k)
+    gq = npu8(q)[:V]
+    gs = s.cpu().numpy()[:V]
+    bad = np.argwhere(gq != rq)
+    assert bad.size == 0, (bad[:5], gq[tuple(bad[0])], rq[tuple(bad[0])])
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    if case == "sweep":
+        # every code the encoder can produce appears
+        assert len(np.unique(gq)) >= 250
+
+
+# ------------------------------------------------------------------------------------ grouped GEMM
+
+def _segments(M, E, V, seed, empty=(1,)):
+    """offsets over M rows with V valid rows, ragged loads, some experts empty."""
+    rng = np.random.default_rng(seed)
+    wts = rng.random(E) + 0.2
+    for e in empty:
+        if e < E:
+            wts[e] = 0
+    cnt = np.floor(wts / wts.sum() * V).astype(np.int64)
+    cnt[np.argmax(wts)] += V - cnt.sum()
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(cnt)
+    assert off[-1] == V
+    return off
+
+
+GEMM_CASES = [
+    # dtype, M, V, E, N, K, epilogue
+    ("bf16", 1000, 900, 6, 400, 200, "silu_mul"),
+    ("bf16", 1000, 1000, 6, 384, 256, "none"),
+    ("bf16", 777, 500, 9, 2 * 456, 712, "silu_mul"),
+    ("bf16", 640, 640, 3, 200, 136, "none"),
+    ("bf16", 300, 0, 4, 128, 64, "silu_mul"),
+    ("f32", 500, 420, 5, 2 * 100, 96, "silu_mul"),
+    ("f32", 500, 500, 5, 132, 68, "none"),
+]
+
+
+@pytest.mark.parametrize("dt,M,V,E,N,K,epi", GEMM_CASES)
+def test_grouped_gemm(dt, M, V, E, N, K, epi):
+    say(f"gemm {dt} M={M} V={V} E={E} N={N} K={K} {epi}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(M + N + K)
+    A = torch.randn(M, K, generator=gen).to(tdt)
+    B = (torch.randn(E, N, K, generator=gen) * 0.05).to(tdt)
+    off = _segments(M, E, V, M + E)
+    g = ops()
+    n_out = N // 2 if epi == "silu_mul" else N
+    C = torch.full((M, n_out), float("nan"), dtype=tdt, device=DEV)
+    g.grouped_gemm(A.to(DEV), B.to(DEV), torch.from_numpy(off).to(DEV), epi, out=C)
+    got = np32(C)
+    ref = ogemm.grouped_gemm(A.float().numpy(), B.float().numpy(), off, epi)
+    assert np.all(got[V:] == 0)
+    err = row_rel_err(got[:V], ref[:V])
+    say(f"  err {err:.3e}")
+    assert err <= TOL[dt]
+    # determinism
+    C2 = torch.empty_like(C)
+    g.grouped_gemm(A.to(DEV), B.to(DEV), torch.from_numpy(off).to(DEV), epi, out=C2)
+    idt = torch.int16 if dt == "bf16" else torch.int32
+    assert torch.equal(C.cpu().view(idt), C2.cpu().view(idt))
+
+
+def test_grouped_gemm_exact_bf16():
+    say("gemm exact bf16")
+    M, E, N, K = 700, 5, 320, 512
+    gen = torch.Generator().manual_seed(11)
+    A = torch.randint(-4, 5, (M, K), generator=gen).to(torch.bfloat16)
+    B = torch.randint(-4, 5, (E, N, K), generator=gen).to(torch.bfloat16)
+    off = _segments(M, E, 650, 12)
+    g = ops()
+    C = g.grouped_gemm(A.to(DEV), B.to(DEV), torch.from_numpy(off).to(DEV), "none", out_dtype=torch.float32)
+    ref = ogemm.grouped_gemm(A.float().numpy(), B.float().numpy(), off)
+    assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
+
+
+def _fp8_operands(M, E, N, K, seed, exact=False):
+    gen = torch.Generator().manual_seed(seed)
+    if exact:
+        a_codes = e4m3.encode(torch.randint(-4, 5, (M, K), generator=gen).float().numpy())
+        a_s = (2.0 ** torch.randint(-2, 3, (M, K // 128), generator=gen).float()).numpy()
+        b_codes = e4m3.encode(torch.randint(-4, 5, (E, N, K), generator=gen).float().numpy())
+        b_s = (2.0 ** torch.randint(-3, 1, (E, N // 128, K // 128), generator=gen).float()).numpy()
+        return a_codes, a_s.astype(np.float32), b_codes, b_s.astype(np.float32)
+    a = torch.randn(M, K, generator=gen) * torch.exp(torch.randn(M, 1, generator=gen))
+    a_codes, a_s = olayer.quant128(a.numpy())
+    bq, bs = [], []
+    for e in range(E):
+        q, s = quantize_weight_blocks(torch.randn(N, K, generator=gen) * 0.02)
+        bq.append(q.view(torch.uint8).numpy())
+        bs.append(s.numpy())
+    return a_codes, a_s, np.stack(bq), np.stack(bs)
+
+
+def _u8_to_fp8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(DEV)
+
+
+@pytest.mark.parametrize("M,V,E,N,K,epi,out", [
+    (600, 520, 5, 512, 384, "silu_mul", "fp8"),
+    (600, 600, 5, 512, 384, "silu_mul", "bf16"),
+    (600, 480, 7, 384, 256, "none", "bf16"),
+    (300, 0, 3, 256, 128, "silu_mul", "fp8"),
+])
+def test_grouped_gemm_fp8(M, V, E, N, K, epi, out):
+    say(f"gemm fp8 M={M} V={V} E={E} N={N} K={K} {epi} -> {out}")
+    aq, as_, bq, bs = _fp8_operands(M, E, N, K, M + N)
+    off = _segments(M, E, V, E + 7)
+    g = ops()
+    odt = torch.float8_e4m3fn if out == "fp8" else torch.bfloat16
+    n_out = N // 2 if epi == "silu_mul" else N
+    C = torch.full((M, n_out), float("nan"), dtype=torch.float32, device=DEV).to(odt)
+    res = g.grouped_gemm(_u8_to_fp8(aq), _u8_to_fp8(bq), torch.from_numpy(off).to(DEV), epi,
+                         a_scales=torch.from_numpy(as_).to(DEV), b_scales=torch.from_numpy(bs).to(DEV),
+                         out_dtype=odt, out=C)
+    if out == "fp8":
+        C, Cs = res
+        gq, gs = npu8(C), Cs.cpu().numpy()
+        rd, rq, rs = ogemm.grouped_gemm(aq, bq, off, epi, as_, bs, out_fp8=True)
+        assert np.all(gq[V:] == 0) and np.all(gs[V:] == 1.0)
+        got = olayer.dequant128(gq, gs)
+        err = row_rel_err(got[:V], rd[:V])
+        say(f"  err {err:.3e}; scale max rel diff {np.abs(gs[:V] / rs[:V] - 1).max() if V else 0:.2e}")
+        assert err <= TOL["fp8"]
+        if V:
+            np.testing.assert_allclose(gs[:V], rs[:V], rtol=1e-5)
+    else:
+        got = np32(C)
+        ref = ogemm.grouped_gemm(aq, bq, off, epi, as_, bs)
+        assert np.all(got[V:] == 0)
+        err = row_rel_err(got[:V], ref[:V])
+        say(f"  err {err:.3e}")
+        assert err <= TOL["fp8"]
+
+
+def test_grouped_gemm_fp8_exact():
+    say("gemm fp8 exact")
+    M, E, N, K = 400, 4, 256, 512
+    aq, as_, bq, bs = _fp8_operands(M, E, N, K, 21, exact=True)
+    off = _segments(M, E, 380, 22)
+    g = ops()
+    C = g.grouped_gemm(_u8_to_fp8(aq), _u8_to_fp8(bq), torch.from_numpy(off).to(DEV), "none",
+                       a_scales=torch.from_numpy(as_).to(DEV), b_scales=torch.from_numpy(bs).to(DEV),
+                       out_dtype=torch.float32)
+    ref = ogemm.grouped_gemm(aq, bq, off, "none", as_, bs)
+    assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
+
+
+# ------------------------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("ydt,odt,H", [(torch.bfloat16, torch.bfloat16, 2880), (torch.float32, torch.float32, 132),
+                                       (torch.bfloat16, torch.float32, 64), (torch.float32, torch.bfloat16, 4)])
+def test_combine(ydt, odt, H):
+    say(f"combine {ydt}->{odt} H={H}")
+    T, E, k = 333, 12, 4
+    ids, w, off, sr, rp = _routing(T, E, k, 1000, 9)
+    R = T * k
+    V = int(off[-1])
+    y = torch.randn(R, H, generator=torch.Generator().manual_seed(10)).to(ydt)
+    y[V:] = float("nan")                                   # sentinel rows are never read
+    g = ops()
+    out = g.unpermute_combine(y.to(DEV), torch.from_numpy(rp).to(DEV), torch.from_numpy(w).to(DEV),
+                              torch.from_numpy(off).to(DEV), k, out_dtype=odt)
+    got = np32(out)
+    ref = olayer.combine(y.float().numpy().astype(np.float64), rp, ids.reshape(-1), w.reshape(-1), T, k, E)
+    dead = (np.arange(T) * k) >= V
+    assert np.all(got[dead] == 0)
+    tol = 1e-2 if odt == torch.bfloat16 else 1e-5
+    assert row_rel_err(got[~dead], ref[~dead]) <= tol

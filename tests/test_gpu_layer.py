@@ -1,0 +1,161 @@
+"""Whole-layer parity (moe_forward through the C ABI) against the oracle.
+
+Small variants of every workload run whole through the oracle (element by
+element); the full-size workloads, in the launch configuration the benchmark
+times, are checked on routing/offsets/permutation (bit-exact, all rows) and on
+sampled tokens the oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import TOL, HostExperts, np32, row_rel_err, say
+from oracle import layer as olayer, routing as orouting
+from oracle.layer import ExpertWeights
+from workloads import generate, get_config, small_variant
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# Reduced-width variants: same E, k, routing structure and dtype; widths keep
+# ragged tails for the 64/128-column tiles and the 128-byte K slices.
+SMALL = {
+    "tiny_f32": dict(T=64),
+    "gptoss20b_bf16": dict(T=512, H=712, I=456),
+    "sweep_bf16_v16384": dict(T=256, H=512, I=192),
+    "sweep_bf16_v8192": dict(T=256, H=512, I=192),
+    "sweep_bf16_v2048": dict(T=256, H=512, I=192),
+    "mixtral8x7b_bf16": dict(T=512, H=384, I=1408),
+    "deepseekv3_fp8": dict(T=256, H=512, I=256, E=32),
+}
+
+
+def _small_cfg(name):
+    base = get_config(name)
+    kw = dict(SMALL[name])
+    cfg = small_variant(base, kw.pop("T"))
+    return cfg.replace(**kw)
+
+
+def _weights_host(inp):
+    if inp.cfg.dtype == "fp8":
+        return ExpertWeights(HostExperts(inp.w13), HostExperts(inp.w2),
+                             inp.w13_scale.cpu().numpy(), inp.w2_scale.cpu().numpy())
+    return ExpertWeights(HostExperts(inp.w13), HostExperts(inp.w2))
+
+
+def _run(inp, **kw):
+    import grouped_gemm_histogram_amd as g
+    cfg = inp.cfg
+    out, aux = g.forward(inp.x, inp.logits, inp.w13, inp.w2, cfg.k, cfg.num_valid_rows,
+                         cfg.renormalize, inp.w13_scale, inp.w2_scale, return_aux=True, **kw)
+    torch.cuda.synchronize()
+    return out, aux
+
+
+def _check_routing(aux, ref):
+    assert np.array_equal(aux.topk_ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_allclose(aux.topk_weights.cpu().numpy(), ref["w"], rtol=1e-5, atol=1e-7)
+    assert np.array_equal(aux.offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(aux.sorted_rows.cpu().numpy(), ref["sorted_rows"])
+    assert np.array_equal(aux.row_pos.cpu().numpy(), ref["row_pos"])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name):
+    cfg = _small_cfg(name)
+    say(f"layer small {cfg}")
+    inp = generate(cfg, "cpu")
+    dev = inp.to(DEV)
+    out, aux = _run(dev)
+    ref = olayer.forward(np32(inp.x), inp.logits.numpy(), _weights_host(inp), cfg.k,
+                         cfg.num_valid_rows, cfg.renormalize)
+    _check_routing(aux, ref)
+    got = np32(out)
+    dead = np.all(ref["out"] == 0, axis=1)
+    assert np.all(got[dead] == 0)
+    err = row_rel_err(got[~dead], ref["out"][~dead])
+    say(f"  max row-relative error {err:.3e} (tolerance {TOL[cfg.dtype]})")
+    assert err <= TOL[cfg.dtype]
+    # determinism: a second run is bitwise identical
+    out2, _ = _run(dev)
+    assert torch.equal(out.cpu().view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
+                       out2.cpu().view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
+
+
+def test_layer_sentinel_poison():
+    """NaN in the inputs of all-sentinel tokens and in every output/workspace byte changes nothing."""
+    cfg = _small_cfg("sweep_bf16_v2048")
+    say(f"layer poison {cfg}")
+    inp = generate(cfg, "cpu").to(DEV)
+    import grouped_gemm_histogram_amd as g
+    base, _ = _run(inp)
+    V = cfg.V
+    x = inp.x.clone()
+    x[(V + cfg.k - 1) // cfg.k:] = float("nan")
+    need = g.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, inp.w13.dtype)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(base, float("nan"))
+    g.forward(x, inp.logits, inp.w13, inp.w2, cfg.k, cfg.num_valid_rows, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    dead = torch.arange(cfg.T, device=DEV) * cfg.k >= V
+    assert (out[dead] == 0).all()
+    assert torch.equal(out[~dead].view(torch.int16), base[~dead].view(torch.int16))
+
+
+def test_layer_no_valid_rows():
+    cfg = _small_cfg("gptoss20b_bf16").replace(num_valid_rows=0)
+    inp = generate(cfg, "cpu").to(DEV)
+    out, aux = _run(inp)
+    assert (out == 0).all()
+    assert aux.offsets.cpu().tolist() == [0] * (cfg.E + 1)
+
+
+def test_layer_top1_unit_weight_is_expert_ffn():
+    cfg = _small_cfg("mixtral8x7b_bf16").replace(k=1)
+    say(f"layer top-1 {cfg}")
+    inp = generate(cfg, "cpu")
+    out, aux = _run(inp.to(DEV))
+    assert (aux.topk_weights == 1.0).all()
+    W = _weights_host(inp)
+    ids = aux.topk_ids.cpu().numpy()
+    x = np32(inp.x)
+    ref = np.zeros((cfg.T, cfg.H))
+    for e in range(cfg.E):
+        rows = np.nonzero(ids[:, 0] == e)[0]
+        if rows.size:
+            ref[rows] = olayer.expert_h(x[rows].astype(np.float64), W.gate_up(e), cfg.I) @ W.down(e).T
+    assert row_rel_err(np32(out), ref) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------------------ full size
+
+FULL = ["gptoss20b_bf16", "sweep_bf16_v16384", "sweep_bf16_v8192", "sweep_bf16_v2048",
+        "mixtral8x7b_bf16", "deepseekv3_fp8"]
+SAMPLES = {"deepseekv3_fp8": 4, "mixtral8x7b_bf16": 12}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_full_size_sampled(name):
+    cfg = get_config(name)
+    say(f"layer full {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} V={cfg.V}")
+    inp = generate(cfg, DEV)
+    out, aux = _run(inp)
+    logits = inp.logits.cpu().numpy()
+    ids, w = orouting.route_topk(logits, cfg.k, cfg.num_valid_rows, cfg.renormalize)
+    off, sr, rp = orouting.build_offsets(ids.reshape(-1), cfg.E)
+    _check_routing(aux, dict(ids=ids, w=w, offsets=off, sorted_rows=sr, row_pos=rp))
+    assert int(off[-1]) == cfg.V
+    got = np32(out)
+    dead = (np.arange(cfg.T) * cfg.k) >= cfg.V
+    assert np.all(got[dead] == 0)
+    live = np.nonzero(~dead)[0]
+    rng = np.random.default_rng(0)
+    n = SAMPLES.get(name, 24)
+    pick = np.unique(np.concatenate([live[:2], live[-2:], rng.choice(live, n, replace=False)]))
+    x_rows = np32(inp.x[torch.from_numpy(pick).to(DEV)])
+    ref = olayer.sampled_outputs(x_rows, ids[pick], w[pick], _weights_host(inp))
+    err = row_rel_err(got[pick], ref)
+    say(f"  {len(pick)} sampled tokens: max row-relative error {err:.3e}")
+    assert err <= TOL[cfg.dtype]

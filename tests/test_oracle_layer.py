@@ -185,3 +185,14 @@ def test_quant128_properties():
     rel = np.abs(d - v) / np.repeat(s, 128, axis=1)
     assert rel.max() <= 16.0          # half an e4m3 ulp at the top binade (32) in scale units
     np.testing.assert_allclose(np.abs(d).reshape(5, 3, 128).max(-1)[nz], amax[nz], rtol=1e-6)
+
+
+def test_sampled_outputs_match_forward():
+    rng = np.random.default_rng(14)
+    for fp8 in (False, True):
+        x, lg, a, b, sa, sb = _rand_layer(rng, 9, 128, 128, 4, fp8=fp8)
+        W = ExpertWeights(a, b, sa, sb)
+        res = layer.forward(x, lg, W, 3, 20)
+        pick = np.array([0, 4, 8, 6])
+        o = layer.sampled_outputs(x[pick], res["ids"][pick], res["w"][pick], W)
+        assert rel_err(o, res["out"][pick]) < 1e-12
