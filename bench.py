@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert layer (route -> offsets -> permute -> gate/up GEMM
++ SiLU*up -> down GEMM -> combine) on one MI355X.
+
+One step = one moe_forward call over the whole synthetic batch, inputs already
+resident in HBM.  Prints one JSON line: layer tokens/s (value), per-stage
+device times from HIP events recorded by the library between its stages, the
+grouped GEMMs' MFMA TFLOP/s against the dense peak, the roofline of the
+dominant kernel (the gate/up GEMM), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload gptoss20b_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE layer tokens/s + grouped-GEMM MFMA TFLOP/s (% peak), gpt-oss-20b shape"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up.json")
+GEMM_SRC = os.path.join(ROOT, "grouped_gemm_histogram_amd", "csrc", "gemm.hip")
+
+
+class HipEvents:
+    """A block of hipEvent_t handles (the library records them on its stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(h)
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per gate/up GEMM launch from committed rocprofv3 counter runs, if still current."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = d.get(workload)
+    if not entry or entry.get("gemm_source_sha") != source_sha():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
+    """The oracle as it stands, on the first ``sample_tokens`` tokens with the full weights."""
+    import numpy as np
+    import torch
+    from oracle import layer as olayer
+    from oracle.layer import ExpertWeights
+
+    S = min(sample_tokens, cfg.T)
+    f32 = lambda t: t.detach().to("cpu", torch.float32).numpy()
+    if cfg.dtype == "fp8":
+        W = ExpertWeights(inp.w13.cpu().view(torch.uint8).numpy(), inp.w2.cpu().view(torch.uint8).numpy(),
+                          inp.w13_scale.cpu().numpy(), inp.w2_scale.cpu().numpy())
+    else:
+        W = ExpertWeights(f32(inp.w13), f32(inp.w2))
+    x = f32(inp.x[:S])
+    lg = inp.logits[:S].cpu().numpy()
+    nv = cfg.num_valid_rows if cfg.num_valid_rows < 0 else min(cfg.num_valid_rows, S * cfg.k)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    olayer.forward(x, lg, W, cfg.k, nv, cfg.renormalize)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"first {S} of {cfg.T} tokens, full weights (float64 per-expert loop)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gptoss20b_bf16")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import grouped_gemm_histogram_amd as g
+    from workloads import generate, get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    g.load()
+    cfg = get_config(args.workload)
+    dev = "cuda:0"
+    inp = generate(cfg, dev)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    need = g.forward_workspace_bytes(T, H, I, E, k, inp.w13.dtype)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty(T, H, dtype=torch.float32 if cfg.dtype == "f32" else torch.bfloat16, device=dev)
+
+    def step(events=None):
+        g.forward(inp.x, inp.logits, inp.w13, inp.w2, k, cfg.num_valid_rows, cfg.renormalize,
+                  inp.w13_scale, inp.w2_scale, out=out, workspace=ws, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nst = len(g._lib.FORWARD_STAGES)
+    ev = HipEvents(args.steps * (nst + 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev.ev[i * (nst + 1):(i + 1) * (nst + 1)])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {}
+    for s, name in enumerate(g._lib.FORWARD_STAGES):
+        stage_ms[name] = sum(ev.ms(i * (nst + 1) + s, i * (nst + 1) + s + 1)
+                             for i in range(args.steps)) / args.steps
+    device_ms = sum(ev.ms(i * (nst + 1), i * (nst + 1) + nst) for i in range(args.steps)) / args.steps
+    ev.close()
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    V = cfg.V
+    esz = 4 if cfg.dtype == "f32" else 2
+    f_gu, f_dn = 4.0 * V * H * I, 2.0 * V * H * I
+    peak = PEAK_TFLOPS[cfg.dtype]
+    gu_tf = f_gu / (stage_ms["gemm_gate_up"] * 1e-3) / 1e12
+    dn_tf = f_dn / (stage_ms["gemm_down"] * 1e-3) / 1e12
+    gemm_tf = (f_gu + f_dn) / ((stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
+    tokens_valid = min(T, -(-V // k))
+    permute_bytes = (tokens_valid + V) * H * (esz if cfg.dtype != "fp8" else 2)
+    combine_bytes = V * H * esz + T * H * esz + 8 * T * k
+    traffic = load_traffic(cfg.name)
+
+    rec = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) hidden states and logits, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": T, "H": H, "I": I, "E": E, "k": k,
+                   "valid_rows": V, "routed_rows": cfg.R},
+        "gemm_tflops": gemm_tf,
+        "gemm_frac_peak": gemm_tf / peak,
+        "gemm_gate_up_tflops": gu_tf,
+        "gemm_down_tflops": dn_tf,
+        "stage_ms": stage_ms,
+        "device_ms_per_step": device_ms,
+        "permute_gbs": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9,
+        "combine_gbs": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
+        "roofline": {"kernel": "grouped_gemm gate/up + SiLU*up", "bound": "mfma",
+                     "achieved": gu_tf, "peak": peak, "unit": "TFLOP/s", "frac": gu_tf / peak,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -29,7 +29,10 @@ SZ = ctypes.c_size_t
 
 class MoeAux(ctypes.Structure):
     _fields_ = [("topk_ids", P), ("topk_weights", P), ("offsets", P),
-                ("sorted_rows", P), ("row_pos", P)]
+                ("sorted_rows", P), ("row_pos", P), ("stage_events", ctypes.POINTER(P))]
+
+
+FORWARD_STAGES = ("route", "offsets", "permute", "gemm_gate_up", "gemm_down", "combine")
 
 
 # name -> (restype, argtypes); mirrors include/moe.h

@@ -273,27 +273,47 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   int32_t* sorted = (aux && aux->sorted_rows) ? aux->sorted_rows : reinterpret_cast<int32_t*>(ws + L.sorted);
   int32_t* rowpos = (aux && aux->row_pos) ? aux->row_pos : reinterpret_cast<int32_t*>(ws + L.rowpos);
   const long long R = T * k;
+  void** ev = aux ? aux->stage_events : nullptr;
+  auto mark = [&](int i) -> moe_status_t {
+    if (ev && ev[i] && hipEventRecord(static_cast<hipEvent_t>(ev[i]), as_stream(stream)) != hipSuccess)
+      return fail(MOE_ERR_LAUNCH, "hipEventRecord of stage event %d failed", i);
+    return MOE_OK;
+  };
 
   moe_status_t s;
+  if ((s = mark(0))) return s;
   if ((s = moe_route_topk(router_logits, T, E, k, num_valid_rows, renormalize, ids, wts, stream)))
     return s;
+  if ((s = mark(1))) return s;
   if ((s = moe_build_offsets(ids, R, E, offs, sorted, rowpos, ws + L.offws,
                              moe::build_offsets_workspace_bytes(R, E), stream)))
     return s;
-  if (T == 0) return ok();
+  if ((s = mark(2))) return s;
+  if (T == 0) {
+    for (int i = 3; i <= MOE_FORWARD_STAGES; ++i)
+      if ((s = mark(i))) return s;
+    return ok();
+  }
   const moe_dtype_t act = fp8 ? MOE_FP8_E4M3 : w_dtype;
   const moe_dtype_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   float* xps = fp8 ? reinterpret_cast<float*>(ws + L.xps) : nullptr;
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
   if ((s = moe_permute(x, x_dtype, T, H, k, sorted, offs, E, R, ws + L.xp, act, xps, stream)))
     return s;
+  if ((s = mark(3))) return s;
   if ((s = moe_grouped_gemm(ws + L.xp, xps, w13, w13_scales, w_dtype, offs, E, R, 2 * I, H,
                             MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream)))
     return s;
+  if ((s = mark(4))) return s;
   if ((s = moe_grouped_gemm(ws + L.h, hs, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
                             ws + L.y, ydt, nullptr, stream)))
     return s;
-  return moe_unpermute_combine(ws + L.y, ydt, rowpos, wts, offs, E, T, H, k, out, out_dtype, stream);
+  if ((s = mark(5))) return s;
+  if ((s = moe_unpermute_combine(ws + L.y, ydt, rowpos, wts, offs, E, T, H, k, out, out_dtype,
+                                 stream)))
+    return s;
+  if ((s = mark(6))) return s;
+  return ok();
 }
 
 }  // extern "C"

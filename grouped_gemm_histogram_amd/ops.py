@@ -167,8 +167,13 @@ def forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.
             num_valid_rows: int = -1, renormalize: bool = True,
             w13_scale: Optional[torch.Tensor] = None, w2_scale: Optional[torch.Tensor] = None,
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, return_aux: bool = False):
-    """The whole layer: x [T, H], logits f32 [T, E], w13 [E, 2I, H], w2 [E, H, I] -> out [T, H]."""
+            workspace: Optional[torch.Tensor] = None, return_aux: bool = False,
+            stage_events=None):
+    """The whole layer: x [T, H], logits f32 [T, E], w13 [E, 2I, H], w2 [E, H, I] -> out [T, H].
+
+    ``stage_events``: optional sequence of 7 hipEvent_t handles (ints) that the
+    library records before the first stage and after each of the six stages.
+    """
     _need(x, "x", (torch.float32, torch.bfloat16))
     T, H = x.shape
     E, I2, H2 = w13.shape
@@ -192,6 +197,13 @@ def forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.
     _need(workspace, "workspace", torch.uint8, device=dev)
     aux_t = None
     aux_c = None
+    ev_arr = None
+    if stage_events is not None:
+        if len(stage_events) != len(_lib.FORWARD_STAGES) + 1:
+            raise ValueError("stage_events needs one event per stage boundary (7)")
+        ev_arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        aux_c = MoeAux()
+        aux_c.stage_events = ctypes.cast(ev_arr, ctypes.POINTER(ctypes.c_void_p))
     if return_aux:
         R = T * k
         aux_t = ForwardAux(torch.empty(T, k, dtype=torch.int32, device=dev),
@@ -199,9 +211,12 @@ def forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.
                            torch.empty(E + 1, dtype=torch.int32, device=dev),
                            torch.empty(R, dtype=torch.int32, device=dev),
                            torch.empty(R, dtype=torch.int32, device=dev))
-        aux_c = MoeAux(aux_t.topk_ids.data_ptr(), aux_t.topk_weights.data_ptr(),
-                       aux_t.offsets.data_ptr(), aux_t.sorted_rows.data_ptr(),
-                       aux_t.row_pos.data_ptr())
+        aux_c = aux_c or MoeAux()
+        aux_c.topk_ids = aux_t.topk_ids.data_ptr()
+        aux_c.topk_weights = aux_t.topk_weights.data_ptr()
+        aux_c.offsets = aux_t.offsets.data_ptr()
+        aux_c.sorted_rows = aux_t.sorted_rows.data_ptr()
+        aux_c.row_pos = aux_t.row_pos.data_ptr()
     _check(lib.forward(_p(x), _DT[x.dtype], _p(logits), _p(w13), _p(w13_scale) if fp8 else None,
                        _p(w2), _p(w2_scale) if fp8 else None, _DT[w13.dtype], T, H, I, E, k,
                        num_valid_rows, int(bool(renormalize)), _p(out), _DT[out_dtype],

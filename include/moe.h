@@ -184,15 +184,23 @@ moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int
                                    int64_t T, int64_t H, int32_t k, void* out,
                                    moe_dtype_t out_dtype, void* stream);
 
+/* Stages of moe_forward, in launch order. */
+#define MOE_FORWARD_STAGES 6   /* route, offsets, permute, gate/up GEMM, down GEMM, combine */
+
 /* Optional caller-owned storage for the routing intermediates of moe_forward.
  * Each non-NULL pointer is used instead of workspace storage, so the caller
- * can read the values after the stream completes. */
+ * can read the values after the stream completes.
+ * stage_events, when non-NULL, points to MOE_FORWARD_STAGES + 1 hipEvent_t
+ * handles created by the caller: event 0 is recorded on the stream before the
+ * first stage and event i after stage i, so hipEventElapsedTime gives each
+ * stage's device time. */
 typedef struct {
   int32_t* topk_ids;      /* [T*k]  */
   float* topk_weights;    /* [T*k]  */
   int32_t* offsets;       /* [E+1]  */
   int32_t* sorted_rows;   /* [T*k]  */
   int32_t* row_pos;       /* [T*k]  */
+  void** stage_events;    /* [MOE_FORWARD_STAGES + 1] hipEvent_t, or NULL */
 } moe_aux_t;
 
 /* Bytes of device workspace moe_forward needs (routing arrays, permuted

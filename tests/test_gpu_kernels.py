@@ -295,12 +295,23 @@ def test_grouped_gemm_fp8(M, V, E, N, K, epi, out):
         gq, gs = npu8(C), Cs.cpu().numpy()
         rd, rq, rs = ogemm.grouped_gemm(aq, bq, off, epi, as_, bs, out_fp8=True)
         assert np.all(gq[V:] == 0) and np.all(gs[V:] == 1.0)
-        got = olayer.dequant128(gq, gs)
-        err = row_rel_err(got[:V], rd[:V])
-        say(f"  err {err:.3e}; scale max rel diff {np.abs(gs[:V] / rs[:V] - 1).max() if V else 0:.2e}")
-        assert err <= TOL["fp8"]
         if V:
-            np.testing.assert_allclose(gs[:V], rs[:V], rtol=1e-5)
+            # The code is decided in fp32 on both sides, but from h accumulated in
+            # fp32 (GPU) vs float64 (oracle): a value within rounding noise of an
+            # e4m3 midpoint may land one step apart.  Scales follow amax closely.
+            np.testing.assert_allclose(gs[:V], rs[:V], rtol=2e-4)
+            # In scale units (|code value| <= 448): the two codes may differ by one
+            # e4m3 step at that magnitude plus the accumulation noise, which is
+            # relative to the group max (448), not to the value itself.
+            dg, dr = e4m3.decode(gq[:V]), e4m3.decode(rq[:V])
+            mag = np.maximum(np.abs(dg), np.abs(dr))
+            ulp = np.where(mag >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(mag, 2.0 ** -6))) - 3),
+                           2.0 ** -9)
+            diff = np.abs(dg - dr)
+            flips = np.count_nonzero(diff)
+            say(f"  codes that differ: {flips} of {diff.size}; max diff/(ulp + noise) "
+                f"{(diff / (ulp + 448 * 2e-4)).max():.3f}")
+            assert np.all(diff <= ulp + 448 * 2e-4) and flips <= 0.01 * diff.size
     else:
         got = np32(C)
         ref = ogemm.grouped_gemm(aq, bq, off, epi, as_, bs)
