@@ -38,6 +38,8 @@
 //    quantisation group; its |max| is reduced across lanes and waves, then
 //    scale = amax / 448 and codes = RNE(value / scale).
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -73,15 +75,62 @@ struct GemmArgs {
   int n_tiles;  // ceil(N_out / BN_out)
 };
 
+#define MOE_INLINE __attribute__((always_inline))
+
 constexpr int kSliceBytes = 128;  // bytes of K per LDS row
 constexpr int kMaxExperts = 1024;
+
+// Tile shapes (BM, BNB, WM, WN, PF): rows x weight rows per tile, waves along M
+// and N, slices of global loads in flight.  Overridable at compile time.
+#ifndef MOE_TILE_BF16_SILU
+#define MOE_TILE_BF16_SILU 256, 256, 4, 2, 0
+#endif
+#ifndef MOE_TILE_BF16_NONE
+#define MOE_TILE_BF16_NONE 256, 256, 4, 2, 0
+#endif
+#ifndef MOE_TILE_FP8_SILU
+#define MOE_TILE_FP8_SILU 128, 256, 2, 2, 1
+#endif
+#ifndef MOE_TILE_FP8_NONE
+#define MOE_TILE_FP8_NONE 128, 128, 2, 2, 1
+#endif
 
 // Swizzle of the 16-byte chunk index within a 128-byte LDS row.  Rows r and
 // r+8 differ in the low bit, so 16 consecutive rows read at one logical chunk
 // land on 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+// One wave-wide direct global->LDS load: lane i's 16 bytes at base + voff land
+// at LDS byte address lds_addr + 16*i (gfx950 global_load_lds_dwordx4; the LDS
+// address comes from M0).  The wait for it is explicit (s_waitcnt vmcnt), as
+// the compiler does not track this load.  M0 is declared clobbered: the
+// compiler sets M0 right before each of its own uses.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  // readfirstlane yields a signed int: widen through uint32_t so the low half is
+  // zero-extended (a sign-extended low half would corrupt the upper address bits)
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(lo | (hi << 32));
+}
+
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWRows = BM / WM;            // activation rows per wave
@@ -98,6 +147,12 @@ struct GemmCfg {
   static_assert(!SILU || kSNB % 2 == 0, "SiLU needs gate and up subtiles in every wave");
   static_assert((BM * 8) % kThreads == 0 && (BNB * 8) % kThreads == 0, "loader mismatch");
   static_assert(kThreads / 8 % 16 == 0, "loader rows must keep the swizzle phase");
+  static_assert(PF >= 0 && PF <= 2, "PF: 0 = direct-to-LDS loads, 1/2 = register prefetch depth");
+  static constexpr int kNW = WM * WN;
+  static constexpr int kDmaA = BM / 8 / kNW;       // direct loads per wave per slice (8 rows each)
+  static constexpr int kDmaB = BNB / 8 / kNW;
+  static_assert(PF != 0 || (BM % (16 * kNW) == 0 && BNB % (16 * kNW) == 0),
+                "direct loads need an even number of 8-row groups per wave");
   static_assert(CT != CType::FP8 || (SILU && kBNOut == 128), "fp8 output needs 128-column tiles");
 };
 
@@ -107,9 +162,9 @@ __device__ __forceinline__ int slab_col(int s, int ii) {
   return 4 * SN * (ii >> 2) + 4 * s + (ii & 3);
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF>;
   using Tr = AbTraits<AB>;
   constexpr int THREADS = Cfg::kThreads;
   constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
@@ -129,7 +184,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int* __restrict__ offsets = args.offsets;
   // offsets as read from memory, clamped to [0, M_rows] so that no row index
   // can leave A or C even for inconsistent input
-  auto off_at = [&](int e) { return min(max(offsets[e], 0), args.M_rows); };
+  auto off_at = [&](int e) MOE_INLINE { return min(max(offsets[e], 0), args.M_rows); };
 
   // ---- per-expert m-tile prefix (wave 0, serial per lane + shuffle scan)
   if (wave == 0) {
@@ -179,6 +234,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   // fragment read geometry
   const int rd_swz = swz(ii);
 
+  int gk = 0;   // slices this workgroup has consumed (direct-load stage parity)
   for (int tile = slot; tile < total_tiles; tile += G) {
     // ---- decode tile -> (expert, n-tile, m-tile)
     const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
@@ -197,14 +253,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     const int rows_valid = min(BM, seg_end - m0);
     const int n0 = nt * Cfg::kBNOut;
 
-    // ---- global source rows of this thread's chunks
-    const uint8_t* a_src[Cfg::kAIters];
+    // ---- byte offsets of this thread's source rows (A from its base, B from the expert's slab)
+    uint32_t a_off[Cfg::kAIters];
 #pragma unroll
     for (int i = 0; i < Cfg::kAIters; ++i) {
       const int r = min(m0 + ld_row0 + i * LD_ROW_STEP, seg_end - 1);
-      a_src[i] = args.A + (long long)r * lda + ld_ch * 16;
+      a_off[i] = (uint32_t)r * (uint32_t)k_bytes;
     }
-    const uint8_t* b_src[Cfg::kBIters];
+    uint32_t b_off[Cfg::kBIters];
     const uint8_t* b_exp = args.B + (long long)e * args.N * lda;
 #pragma unroll
     for (int i = 0; i < Cfg::kBIters; ++i) {
@@ -218,31 +274,35 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const int within = qq % SLAB;
       const int col = n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15);
       const int colc = min(col, N_out - 1);
-      b_src[i] = b_exp + (long long)(half * N_out + colc) * lda + ld_ch * 16;
+      b_off[i] = (uint32_t)(half * N_out + colc) * (uint32_t)k_bytes;
     }
 
-    uint4 a_reg[Cfg::kAIters], b_reg[Cfg::kBIters];
-    auto load_slice = [&](int kt) {
-      const int kb = kt * kSliceBytes + ld_ch * 16;
-      const bool in = kb < k_bytes;
+    // Global loads always use an in-bounds address (the last chunk of the row
+    // for chunks past K); such chunks are replaced by zeros when stored to LDS.
+    auto load_to = [&](uint4(&ra)[Cfg::kAIters], uint4(&rb)[Cfg::kBIters], int kt) MOE_INLINE {
+      const int kb = min(kt * kSliceBytes + ld_ch * 16, k_bytes - 16);
 #pragma unroll
       for (int i = 0; i < Cfg::kAIters; ++i)
-        a_reg[i] = in ? *reinterpret_cast<const uint4*>(a_src[i] + kt * kSliceBytes)
-                      : make_uint4(0, 0, 0, 0);
+        ra[i] = *reinterpret_cast<const uint4*>(args.A + a_off[i] + kb);
 #pragma unroll
       for (int i = 0; i < Cfg::kBIters; ++i)
-        b_reg[i] = in ? *reinterpret_cast<const uint4*>(b_src[i] + kt * kSliceBytes)
-                      : make_uint4(0, 0, 0, 0);
+        rb[i] = *reinterpret_cast<const uint4*>(b_exp + b_off[i] + kb);
     };
-    auto store_slice = [&](int buf) {
+    auto store_from = [&](const uint4(&ra)[Cfg::kAIters], const uint4(&rb)[Cfg::kBIters], int buf,
+                          int kt) MOE_INLINE {
+      // all-ones when the chunk lies inside K, else zero (a mask keeps the arrays in registers)
+      const uint32_t keep = (kt * kSliceBytes + ld_ch * 16 < k_bytes) ? 0xffffffffu : 0u;
+      auto masked = [keep](uint4 v) MOE_INLINE {
+        return make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      };
       uint8_t* base = smem[buf];
 #pragma unroll
       for (int i = 0; i < Cfg::kAIters; ++i)
-        *reinterpret_cast<uint4*>(base + ld_lds + i * LD_ROW_STEP * kSliceBytes) = a_reg[i];
+        *reinterpret_cast<uint4*>(base + ld_lds + i * LD_ROW_STEP * kSliceBytes) = masked(ra[i]);
 #pragma unroll
       for (int i = 0; i < Cfg::kBIters; ++i)
         *reinterpret_cast<uint4*>(base + BM * kSliceBytes + ld_lds + i * LD_ROW_STEP * kSliceBytes) =
-            b_reg[i];
+            masked(rb[i]);
     };
 
     f32x4 acc[SM][SNB];
@@ -268,15 +328,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       bsc = args.b_scales + (long long)e * NB * KB;
     }
 
-    load_slice(0);
-    store_slice(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) load_slice(kt + 1);
-      const uint8_t* sA = smem[cur] + (wm * Cfg::kWRows) * kSliceBytes;
-      const uint8_t* sB = smem[cur] + BM * kSliceBytes;
+    // Activation subtile t of wave wm holds tile rows 16*(t*WM + wm) + [0, 16): the
+    // waves of a column interleave, so a short tile still spreads over all of them.
+    // FULL = every subtile has valid rows; otherwise subtiles past rows_valid skip
+    // their LDS reads and MFMAs.
+    auto compute = [&](auto full_tag, int buf, int kt, bool k_tail) MOE_INLINE {
+      constexpr bool FULL = decltype(full_tag)::value;
+      const uint8_t* sA = smem[buf];
+      const uint8_t* sB = smem[buf] + BM * kSliceBytes;
+      bool live[SM];
+#pragma unroll
+      for (int t = 0; t < SM; ++t) live[t] = FULL || 16 * (t * WM + wm) < rows_valid;
 
       float afac[SM][2];
       if constexpr (AB == AbType::FP8) {
@@ -284,7 +346,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         const float sb1 = bsc[nb_half[1] * KB + kt];
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
-          const int r = min(m0 + wm * Cfg::kWRows + 16 * t + ii, seg_end - 1);
+          const int r = min(m0 + 16 * (t * WM + wm) + ii, seg_end - 1);
           const float sa = args.a_scales[(long long)r * KB + kt];
           afac[t][0] = sa * sb0;
           afac[t][1] = sa * sb1;
@@ -299,9 +361,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           const int ch = (Tr::kChunksPerLane == 1) ? (step * 4 + g) : (2 * g + c);
           const int coff = (ch ^ rd_swz) << 4;
 #pragma unroll
-          for (int t = 0; t < SM; ++t)
-            af[t][c] = *reinterpret_cast<const uint4*>(sA + (16 * t + ii) * kSliceBytes + coff);
-#pragma unroll
           for (int s = 0; s < SNB; ++s) {
             int wrow;
             if constexpr (SILU) {
@@ -312,9 +371,22 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             }
             wf[s][c] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
           }
+#pragma unroll
+          for (int t = 0; t < SM; ++t)
+            if (live[t])
+              af[t][c] = *reinterpret_cast<const uint4*>(sA + (16 * (t * WM + wm) + ii) * kSliceBytes + coff);
+          if (k_tail) {
+            // chunks past K hold copies of the row's last chunk: zero the activation side
+            const uint32_t keep = (kt * kSliceBytes + ch * 16 < k_bytes) ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int t = 0; t < SM; ++t)
+              af[t][c] = make_uint4(af[t][c].x & keep, af[t][c].y & keep, af[t][c].z & keep,
+                                    af[t][c].w & keep);
+          }
         }
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
+          if (!live[t]) continue;
 #pragma unroll
           for (int s = 0; s < SNB; ++s) {
             if constexpr (AB == AbType::BF16) {
@@ -342,16 +414,106 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           }
         }
       }
+    };
 
-      if (kt + 1 < KT) store_slice(cur ^ 1);
-      __syncthreads();
-    }
+    // ---- K loop: LDS double buffer fed from registers, PF slices of loads in flight
+    auto k_loop = [&](auto full_tag) MOE_INLINE {
+      if constexpr (PF == 0) {
+        // Direct global->LDS loads, two LDS stages.  The stage of a slice follows
+        // the workgroup's running slice count gk, so the first slice of the next
+        // tile never lands in the stage other waves may still be reading.
+        const uint8_t* a_u = uniform_ptr(args.A);
+        const uint8_t* b_u = uniform_ptr(b_exp);
+        const uint32_t wave_u = uniform_u32((uint32_t)wave);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&smem[0][0];
+        const uint32_t cc0 = 16u * ((lane & 7) ^ (lane >> 3));   // logical chunk, even 8-row group
+        const uint32_t cc1 = cc0 ^ 16u;                           // odd 8-row group
+        uint32_t rowA[Cfg::kDmaA], rowB[Cfg::kDmaB];
+#pragma unroll
+        for (int j = 0; j < Cfg::kDmaA; ++j) {
+          const int r = (wave * Cfg::kDmaA + j) * 8 + (lane >> 3);
+          rowA[j] = (uint32_t)min(m0 + r, seg_end - 1) * (uint32_t)k_bytes;
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::kDmaB; ++j) {
+          const int qrow = (wave * Cfg::kDmaB + j) * 8 + (lane >> 3);
+          int half = 0, qq = qrow;
+          if constexpr (SILU) {
+            half = qrow / Cfg::kBNOut;
+            qq = qrow - half * Cfg::kBNOut;
+          }
+          constexpr int SLAB = Cfg::kWNOut;
+          const int within = qq % SLAB;
+          const int col = min(n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
+          rowB[j] = (uint32_t)(half * N_out + col) * (uint32_t)k_bytes;
+        }
+        auto issue = [&](int kt, int stage) MOE_INLINE {
+          const uint32_t kb = (uint32_t)(kt * kSliceBytes);
+          const uint32_t last = (uint32_t)(k_bytes - 16);
+          const uint32_t o0 = min(kb + cc0, last), o1 = min(kb + cc1, last);
+          const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kTileBytes;
+#pragma unroll
+          for (int j = 0; j < Cfg::kDmaA; ++j)
+            dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + ((j & 1) ? o1 : o0));
+#pragma unroll
+          for (int j = 0; j < Cfg::kDmaB; ++j)
+            dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, b_u,
+                  rowB[j] + ((j & 1) ? o1 : o0));
+        };
+        const bool has_tail = (k_bytes % kSliceBytes) != 0;
+        issue(0, gk & 1);
+        for (int kt = 0; kt < KT; ++kt) {
+          wait_all_vm();
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (kt + 1 < KT) issue(kt + 1, (gk + 1) & 1);
+          compute(full_tag, gk & 1, kt, has_tail && kt == KT - 1);
+          ++gk;
+        }
+        return;
+      }
+      uint4 ra0[Cfg::kAIters], rb0[Cfg::kBIters];
+      if constexpr (PF == 1) {
+        load_to(ra0, rb0, 0);
+        store_from(ra0, rb0, 0, 0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; ++kt) {
+          if (kt + 1 < KT) load_to(ra0, rb0, kt + 1);
+          compute(full_tag, kt & 1, kt, false);
+          if (kt + 1 < KT) store_from(ra0, rb0, (kt + 1) & 1, kt + 1);
+          __syncthreads();
+        }
+      } else {
+        uint4 ra1[Cfg::kAIters], rb1[Cfg::kBIters];
+        load_to(ra0, rb0, 0);
+        if (KT > 1) load_to(ra1, rb1, 1);
+        store_from(ra0, rb0, 0, 0);
+        __syncthreads();
+        for (int kt = 0; kt < KT; kt += 2) {
+          // slice kt is in LDS buffer 0; slice kt+1 is in flight in set 1
+          if (kt + 2 < KT) load_to(ra0, rb0, kt + 2);
+          compute(full_tag, 0, kt, false);
+          if (kt + 1 < KT) store_from(ra1, rb1, 1, kt + 1);
+          __syncthreads();
+          if (kt + 1 >= KT) break;
+          // slice kt+1 is in LDS buffer 1; slice kt+2 is in flight in set 0
+          if (kt + 3 < KT) load_to(ra1, rb1, kt + 3);
+          compute(full_tag, 1, kt + 1, false);
+          if (kt + 2 < KT) store_from(ra0, rb0, 0, kt + 2);
+          __syncthreads();
+        }
+      }
+    };
+    if (rows_valid >= BM)
+      k_loop(std::integral_constant<bool, true>{});
+    else
+      k_loop(std::integral_constant<bool, false>{});
 
-    // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of rows 16t + ii
+    // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of tile row 16*(t*WM+wm) + ii
     const int cbase = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
 #pragma unroll
     for (int t = 0; t < SM; ++t) {
-      const int rloc = wm * Cfg::kWRows + 16 * t + ii;
+      const int rloc = 16 * (t * WM + wm) + ii;
       const bool row_ok = rloc < rows_valid;
       const long long m = (long long)m0 + rloc;
       float v[4 * SNO];
@@ -453,12 +615,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF>;
   GemmArgs a = a0;
   a.n_tiles = (a.N_out + Cfg::kBNOut - 1) / Cfg::kBNOut;
-  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN>;
+  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF>;
   static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::kThreads, 0) != hipSuccess || n <= 0)
@@ -490,28 +652,28 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
   if (p.ab_dtype == 1) {
     if (p.silu) {
-      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, 128, 128, 2, 2>(a, stream);
-      return launch_cfg<AbType::BF16, CType::F32, true, 128, 128, 2, 2>(a, stream);
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU>(a, stream);
     }
-    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, 128, 128, 2, 2>(a, stream);
-    return launch_cfg<AbType::BF16, CType::F32, false, 128, 128, 2, 2>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE>(a, stream);
   }
   if (p.ab_dtype == 0) {
     if (p.silu) {
-      if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, true, 64, 64, 2, 2>(a, stream);
-      return launch_cfg<AbType::F32, CType::F32, true, 64, 64, 2, 2>(a, stream);
+      if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, true, 64, 64, 2, 2, 1>(a, stream);
+      return launch_cfg<AbType::F32, CType::F32, true, 64, 64, 2, 2, 1>(a, stream);
     }
-    if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, false, 64, 64, 2, 2>(a, stream);
-    return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, false, 64, 64, 2, 2, 1>(a, stream);
+    return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2, 1>(a, stream);
   }
   // fp8 operands
   if (p.silu) {
-    if (p.c_dtype == 2) return launch_cfg<AbType::FP8, CType::FP8, true, 128, 256, 2, 2>(a, stream);
-    if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, true, 128, 256, 2, 2>(a, stream);
-    return launch_cfg<AbType::FP8, CType::F32, true, 128, 256, 2, 2>(a, stream);
+    if (p.c_dtype == 2) return launch_cfg<AbType::FP8, CType::FP8, true, MOE_TILE_FP8_SILU>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, true, MOE_TILE_FP8_SILU>(a, stream);
+    return launch_cfg<AbType::FP8, CType::F32, true, MOE_TILE_FP8_SILU>(a, stream);
   }
-  if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, false, 128, 128, 2, 2>(a, stream);
-  return launch_cfg<AbType::FP8, CType::F32, false, 128, 128, 2, 2>(a, stream);
+  if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, false, MOE_TILE_FP8_NONE>(a, stream);
+  return launch_cfg<AbType::FP8, CType::F32, false, MOE_TILE_FP8_NONE>(a, stream);
 }
 
 }  // namespace moe
