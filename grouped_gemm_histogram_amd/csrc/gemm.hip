@@ -80,25 +80,27 @@ struct GemmArgs {
 constexpr int kSliceBytes = 128;  // bytes of K per LDS row
 constexpr int kMaxExperts = 1024;
 
-// Tile shapes (BM, BNB, WM, WN, PF): rows x weight rows per tile, waves along M
-// and N, slices of global loads in flight.  Overridable at compile time.
+// Tile shapes (BM, BNB, WM, WN, PF, ST): rows x weight rows per tile, waves along
+// M and N, loader (PF = 0: direct global->LDS loads; 1 or 2: slices prefetched
+// through registers) and LDS stages.  Overridable at compile time.
 #ifndef MOE_TILE_BF16_SILU
-#define MOE_TILE_BF16_SILU 256, 256, 4, 2, 0
+#define MOE_TILE_BF16_SILU 192, 192, 4, 2, 0, 3
 #endif
 #ifndef MOE_TILE_BF16_NONE
-#define MOE_TILE_BF16_NONE 256, 256, 4, 2, 0
+#define MOE_TILE_BF16_NONE 192, 192, 4, 2, 0, 3
 #endif
 #ifndef MOE_TILE_FP8_SILU
-#define MOE_TILE_FP8_SILU 128, 256, 2, 2, 1
+#define MOE_TILE_FP8_SILU 128, 256, 2, 2, 1, 2
 #endif
 #ifndef MOE_TILE_FP8_NONE
-#define MOE_TILE_FP8_NONE 128, 128, 2, 2, 1
+#define MOE_TILE_FP8_NONE 128, 128, 2, 2, 1, 2
 #endif
 
-// Swizzle of the 16-byte chunk index within a 128-byte LDS row.  Rows r and
-// r+8 differ in the low bit, so 16 consecutive rows read at one logical chunk
-// land on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Swizzle of the 16-byte chunk index within a 128-byte LDS row: logical chunk c
+// of row r is stored at chunk c ^ (r & 7).  The MFMA operand fetch (16 rows at
+// one logical chunk per 16 lanes) reads without bank conflicts on gfx950 in
+// this layout (measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // One wave-wide direct global->LDS load: lane i's 16 bytes at base + voff land
 // at LDS byte address lds_addr + 16*i (gfx950 global_load_lds_dwordx4; the LDS
@@ -130,7 +132,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>(lo | (hi << 32));
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWRows = BM / WM;            // activation rows per wave
@@ -151,8 +153,10 @@ struct GemmCfg {
   static constexpr int kNW = WM * WN;
   static constexpr int kDmaA = BM / 8 / kNW;       // direct loads per wave per slice (8 rows each)
   static constexpr int kDmaB = BNB / 8 / kNW;
-  static_assert(PF != 0 || (BM % (16 * kNW) == 0 && BNB % (16 * kNW) == 0),
-                "direct loads need an even number of 8-row groups per wave");
+  static_assert(PF != 0 || (BM % (8 * kNW) == 0 && BNB % (8 * kNW) == 0),
+                "direct loads need whole 8-row groups per wave");
+  static_assert(ST == 2 || (PF == 0 && ST == 3), "LDS stages: 2, or 3 with direct loads");
+  static constexpr int kDmaPerSlice = kDmaA + kDmaB;
   static_assert(CT != CType::FP8 || (SILU && kBNOut == 128), "fp8 output needs 128-column tiles");
 };
 
@@ -162,14 +166,14 @@ __device__ __forceinline__ int slab_col(int s, int ii) {
   return 4 * SN * (ii >> 2) + 4 * s + (ii & 3);
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
   using Tr = AbTraits<AB>;
   constexpr int THREADS = Cfg::kThreads;
   constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][Cfg::kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST][Cfg::kTileBytes];
   __shared__ int s_mt_pre[kMaxExperts + 1];
   __shared__ float s_red[(CT == CType::FP8) ? WN * BM : 1];
 
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   // fragment read geometry
   const int rd_swz = swz(ii);
 
-  int gk = 0;   // slices this workgroup has consumed (direct-load stage parity)
+  int gk = 0;   // slices this workgroup has consumed (selects the direct-load stage)
   for (int tile = slot; tile < total_tiles; tile += G) {
     // ---- decode tile -> (expert, n-tile, m-tile)
     const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // waves of a column interleave, so a short tile still spreads over all of them.
     // FULL = every subtile has valid rows; otherwise subtiles past rows_valid skip
     // their LDS reads and MFMAs.
-    auto compute = [&](auto full_tag, int buf, int kt, bool k_tail) MOE_INLINE {
+    auto compute = [&](auto full_tag, int buf, int kt, bool k_tail, auto&& hook) MOE_INLINE {
       constexpr bool FULL = decltype(full_tag)::value;
       const uint8_t* sA = smem[buf];
       const uint8_t* sB = smem[buf] + BM * kSliceBytes;
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         }
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
+          if (t > 0 || step > 0) hook(step * SM + t - 1);   // between rows of MFMAs
           if (!live[t]) continue;
 #pragma unroll
           for (int s = 0; s < SNB; ++s) {
@@ -414,20 +419,23 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           }
         }
       }
+      hook(Tr::kSteps * SM - 1);
     };
 
     // ---- K loop: LDS double buffer fed from registers, PF slices of loads in flight
     auto k_loop = [&](auto full_tag) MOE_INLINE {
       if constexpr (PF == 0) {
-        // Direct global->LDS loads, two LDS stages.  The stage of a slice follows
-        // the workgroup's running slice count gk, so the first slice of the next
-        // tile never lands in the stage other waves may still be reading.
+        // Direct global->LDS loads into ST LDS stages, ST-1 slices in flight.  The
+        // stage of a slice follows the workgroup's running slice count gk, so the
+        // first slices of the next tile never land in a stage that other waves
+        // may still be reading.
         const uint8_t* a_u = uniform_ptr(args.A);
         const uint8_t* b_u = uniform_ptr(b_exp);
         const uint32_t wave_u = uniform_u32((uint32_t)wave);
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&smem[0][0];
-        const uint32_t cc0 = 16u * ((lane & 7) ^ (lane >> 3));   // logical chunk, even 8-row group
-        const uint32_t cc1 = cc0 ^ 16u;                           // odd 8-row group
+        // lane i of a load fills row i/8 of an 8-row group at physical chunk i%8,
+        // i.e. logical chunk (i%8) ^ swz(row) = (i%8) ^ (i/8)
+        const uint32_t cc = 16u * ((lane & 7) ^ (lane >> 3));
         uint32_t rowA[Cfg::kDmaA], rowB[Cfg::kDmaB];
 #pragma unroll
         for (int j = 0; j < Cfg::kDmaA; ++j) {
@@ -447,29 +455,55 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           const int col = min(n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
           rowB[j] = (uint32_t)(half * N_out + col) * (uint32_t)k_bytes;
         }
-        auto issue = [&](int kt, int stage) MOE_INLINE {
-          const uint32_t kb = (uint32_t)(kt * kSliceBytes);
-          const uint32_t last = (uint32_t)(k_bytes - 16);
-          const uint32_t o0 = min(kb + cc0, last), o1 = min(kb + cc1, last);
+        // load j of this wave for slice kt (j < kDmaA: activation rows, else weight rows)
+        auto issue_one = [&](int j, int kt, int stage) MOE_INLINE {
+          const uint32_t o = min((uint32_t)(kt * kSliceBytes) + cc, (uint32_t)(k_bytes - 16));
           const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kTileBytes;
+          if (j < Cfg::kDmaA)
+            dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + o);
+          else
+            dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + (j - Cfg::kDmaA)) * 1024u, b_u,
+                  rowB[j - Cfg::kDmaA] + o);
+        };
+        auto issue = [&](int kt, int stage) MOE_INLINE {
 #pragma unroll
-          for (int j = 0; j < Cfg::kDmaA; ++j)
-            dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + ((j & 1) ? o1 : o0));
-#pragma unroll
-          for (int j = 0; j < Cfg::kDmaB; ++j)
-            dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, b_u,
-                  rowB[j] + ((j & 1) ? o1 : o0));
+          for (int j = 0; j < Cfg::kDmaPerSlice; ++j) issue_one(j, kt, stage);
         };
         const bool has_tail = (k_bytes % kSliceBytes) != 0;
-        issue(0, gk & 1);
+        int st = gk % ST;                       // stage of slice kt
+        issue(0, st);
+        if constexpr (ST == 3) {
+          if (KT > 1) issue(1, st == 2 ? 0 : st + 1);
+        }
         for (int kt = 0; kt < KT; ++kt) {
-          wait_all_vm();
+          // slice kt has landed once at most the loads of later slices are outstanding
+          if constexpr (ST == 3) {
+            if (kt + 1 < KT)
+              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
+            else
+              wait_all_vm();
+          } else {
+            wait_all_vm();
+          }
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          if (kt + 1 < KT) issue(kt + 1, (gk + 1) & 1);
-          compute(full_tag, gk & 1, kt, has_tail && kt == KT - 1);
-          ++gk;
+          // The next slice's loads are spread between the rows of MFMAs, so no
+          // wave stalls on load issue before its first MFMA.
+          const bool more = kt + ST - 1 < KT;
+          int nxt = st + ST - 1;
+          if (nxt >= ST) nxt -= ST;
+          constexpr int kHooks = Tr::kSteps * SM;
+          auto hook = [&](int h) MOE_INLINE {
+            if (!more) return;
+#pragma unroll
+            for (int j = 0; j < Cfg::kDmaPerSlice; ++j)
+              if (j * kHooks / Cfg::kDmaPerSlice == h) issue_one(j, kt + ST - 1, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          compute(full_tag, st, kt, has_tail && kt == KT - 1, hook);
+          st = (st + 1 == ST) ? 0 : st + 1;
         }
+        gk += KT;
         return;
       }
       uint4 ra0[Cfg::kAIters], rb0[Cfg::kBIters];
@@ -479,7 +513,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         __syncthreads();
         for (int kt = 0; kt < KT; ++kt) {
           if (kt + 1 < KT) load_to(ra0, rb0, kt + 1);
-          compute(full_tag, kt & 1, kt, false);
+          compute(full_tag, kt & 1, kt, false, [](int) {});
           if (kt + 1 < KT) store_from(ra0, rb0, (kt + 1) & 1, kt + 1);
           __syncthreads();
         }
@@ -492,13 +526,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         for (int kt = 0; kt < KT; kt += 2) {
           // slice kt is in LDS buffer 0; slice kt+1 is in flight in set 1
           if (kt + 2 < KT) load_to(ra0, rb0, kt + 2);
-          compute(full_tag, 0, kt, false);
+          compute(full_tag, 0, kt, false, [](int) {});
           if (kt + 1 < KT) store_from(ra1, rb1, 1, kt + 1);
           __syncthreads();
           if (kt + 1 >= KT) break;
           // slice kt+1 is in LDS buffer 1; slice kt+2 is in flight in set 0
           if (kt + 3 < KT) load_to(ra1, rb1, kt + 3);
-          compute(full_tag, 1, kt + 1, false);
+          compute(full_tag, 1, kt + 1, false, [](int) {});
           if (kt + 2 < KT) store_from(ra0, rb0, 0, kt + 2);
           __syncthreads();
         }
@@ -536,7 +570,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, s_red[w2 * BM + rloc]);
         __syncthreads();
         const float scale = (amax == 0.f) ? 1.f : amax / 448.f;
-        if (row_ok && cbase < N_out) {
+        if (row_ok && cbase + 4 * SNO <= N_out) {
           uint32_t wd[SNO];
 #pragma unroll
           for (int s = 0; s < SNO; ++s)
@@ -550,18 +584,25 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       } else if constexpr (CT == CType::BF16) {
         if (row_ok) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(args.C) + m * N_out + cbase;
-          if constexpr (SNO == 1) {
-            if (cbase < N_out)
-              *reinterpret_cast<uint2*>(dst) =
-                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          } else {
+          // 4*SNO contiguous columns, written as 8-column (16-byte) stores where
+          // all 8 columns exist, else as 4-column (8-byte) stores; N_out is a
+          // multiple of 8 and cbase of 4, so every 4-column unit is whole.
 #pragma unroll
-            for (int u = 0; u < SNO / 2; ++u)
-              if (cbase + 8 * u < N_out)
-                *reinterpret_cast<uint4*>(dst + 8 * u) =
-                    make_uint4(pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]),
-                               pack_bf16x2(v[8 * u + 4], v[8 * u + 5]),
-                               pack_bf16x2(v[8 * u + 6], v[8 * u + 7]));
+          for (int u = 0; u < SNO / 2; ++u) {
+            const int c = cbase + 8 * u;
+            const uint2 lo = make_uint2(pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]));
+            const uint2 hi = make_uint2(pack_bf16x2(v[8 * u + 4], v[8 * u + 5]),
+                                        pack_bf16x2(v[8 * u + 6], v[8 * u + 7]));
+            if (c + 8 <= N_out)
+              *reinterpret_cast<uint4*>(dst + 8 * u) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            else if (c + 4 <= N_out)
+              *reinterpret_cast<uint2*>(dst + 8 * u) = lo;
+          }
+          if constexpr (SNO % 2 == 1) {
+            constexpr int u = SNO / 2;
+            if (cbase + 8 * u + 4 <= N_out)
+              *reinterpret_cast<uint2*>(dst + 8 * u) =
+                  make_uint2(pack_bf16x2(v[8 * u], v[8 * u + 1]), pack_bf16x2(v[8 * u + 2], v[8 * u + 3]));
           }
         }
       } else {
@@ -569,7 +610,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           float* dst = reinterpret_cast<float*>(args.C) + m * N_out + cbase;
 #pragma unroll
           for (int s = 0; s < SNO; ++s)
-            if (cbase + 4 * s < N_out)
+            if (cbase + 4 * s + 4 <= N_out)
               *reinterpret_cast<float4*>(dst + 4 * s) =
                   make_float4(v[4 * s], v[4 * s + 1], v[4 * s + 2], v[4 * s + 3]);
         }
@@ -615,12 +656,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
   GemmArgs a = a0;
   a.n_tiles = (a.N_out + Cfg::kBNOut - 1) / Cfg::kBNOut;
-  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF>;
+  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
   static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::kThreads, 0) != hipSuccess || n <= 0)
@@ -660,11 +701,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   }
   if (p.ab_dtype == 0) {
     if (p.silu) {
-      if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, true, 64, 64, 2, 2, 1>(a, stream);
-      return launch_cfg<AbType::F32, CType::F32, true, 64, 64, 2, 2, 1>(a, stream);
+      if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, true, 64, 64, 2, 2, 1, 2>(a, stream);
+      return launch_cfg<AbType::F32, CType::F32, true, 64, 64, 2, 2, 1, 2>(a, stream);
     }
-    if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, false, 64, 64, 2, 2, 1>(a, stream);
-    return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2, 1>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::F32, CType::BF16, false, 64, 64, 2, 2, 1, 2>(a, stream);
+    return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2, 1, 2>(a, stream);
   }
   // fp8 operands
   if (p.silu) {

@@ -208,6 +208,10 @@ GEMM_CASES = [
     ("bf16", 777, 500, 9, 2 * 456, 712, "silu_mul"),
     ("bf16", 640, 640, 3, 200, 136, "none"),
     ("bf16", 300, 0, 4, 128, 64, "silu_mul"),
+    # output widths whose last 12-column run straddles the row end
+    ("bf16", 900, 850, 5, 2 * 1408, 384, "silu_mul"),
+    ("bf16", 700, 700, 3, 1412 - 4, 256, "none"),
+    ("bf16", 500, 480, 4, 2 * 104, 192, "silu_mul"),
     ("f32", 500, 420, 5, 2 * 100, 96, "silu_mul"),
     ("f32", 500, 500, 5, 132, 68, "none"),
 ]
