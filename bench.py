@@ -76,6 +76,56 @@ def load_traffic(workload: str):
     return entry.get("traffic_bytes")
 
 
+def predicted_mfma_flops(offsets, M_rows: int, n_out_total: int, K: int, tile) -> float:
+    """MFMA flops the grouped GEMM executes for these offsets: every expert segment is covered by
+    ceil(M_e / tile_m) tiles in M, each computing 16*ceil(rows/16) rows, by ceil(N_out / n_out)
+    tiles of tile_n weight rows, over ceil(K / k_slice) slices."""
+    tile_m, tile_n, k_slice = tile
+    n_tiles = -(-n_out_total // tile_n)
+    kt = -(-K // k_slice)
+    rows = 0
+    off = [min(max(int(v), 0), M_rows) for v in offsets]
+    for e in range(len(off) - 1):
+        m = off[e + 1] - off[e]
+        while m > 0:
+            r = min(tile_m, m)
+            rows += 16 * (-(-r // 16))
+            m -= r
+    return 2.0 * rows * n_tiles * tile_n * kt * k_slice
+
+
+def clamp_ab(g, cfg, inp, steps: int) -> dict:
+    """Sentinel rows excluded (this layer) vs clamped onto the last expert (the behaviour the
+    transformers PR #45621 write-up, section 2, removes): same output, more GEMM rows."""
+    import torch
+    k, E = cfg.k, cfg.E
+    def staged(clamp: bool):
+        ids, w = g.route_topk(inp.logits, k, cfg.num_valid_rows, cfg.renormalize)
+        if clamp:
+            ids = torch.where(ids >= E, torch.full_like(ids, E - 1), ids)
+        off, sr, rp = g.build_offsets(ids, E)
+        xp = g.permute(inp.x, sr, off, k)
+        h = g.grouped_gemm(xp, inp.w13, off, "silu_mul")
+        y = g.grouped_gemm(h, inp.w2, off, "none")
+        return g.unpermute_combine(y, rp, w, off, k)
+    out = {}
+    for clamp in (False, True):
+        for _ in range(2):
+            o = staged(clamp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            o = staged(clamp)
+        e1.record()
+        torch.cuda.synchronize()
+        out["clamped_ms" if clamp else "excluded_ms"] = e0.elapsed_time(e1) / steps
+        out["out_clamped" if clamp else "out_excluded"] = o
+    same = torch.equal(out.pop("out_clamped").view(torch.int16), out.pop("out_excluded").view(torch.int16))
+    out["outputs_identical"] = bool(same)
+    return out
+
+
 def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
     """The oracle as it stands, on the first ``sample_tokens`` tokens with the full weights."""
     import numpy as np
@@ -114,8 +164,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gptoss20b_bf16")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
+                    help="tokens for the CPU oracle baseline (default: the whole layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clamp-ab", action="store_true",
+                    help="also time the staged layer with sentinel rows clamped onto the last expert")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -145,6 +198,12 @@ def main() -> int:
     def step(events=None):
         g.forward(inp.x, inp.logits, inp.w13, inp.w2, k, cfg.num_valid_rows, cfg.renormalize,
                   inp.w13_scale, inp.w2_scale, out=out, workspace=ws, stage_events=events)
+
+    # offsets of this routing, for the predicted MFMA work (outside the timed region)
+    _, aux = g.forward(inp.x, inp.logits, inp.w13, inp.w2, k, cfg.num_valid_rows, cfg.renormalize,
+                       inp.w13_scale, inp.w2_scale, out=out, workspace=ws, return_aux=True)
+    torch.cuda.synchronize()
+    offsets_host = aux.offsets.cpu().tolist()
 
     for _ in range(args.warmup):
         step()
@@ -184,6 +243,11 @@ def main() -> int:
     permute_bytes = (tokens_valid + V) * H * (esz if cfg.dtype != "fp8" else 2)
     combine_bytes = V * H * esz + T * H * esz + 8 * T * k
     traffic = load_traffic(cfg.name)
+    R = cfg.R
+    pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none"))
+    # SiLU*up tiles hold tile_n/2 output columns: count them against N_out = I
+    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul")
+    pred_gu = predicted_mfma_flops(offsets_host, R, I, H, (tm, tn // 2, ks)) * 2
 
     rec = {
         "metric": METRIC,
@@ -208,10 +272,14 @@ def main() -> int:
         "device_ms_per_step": device_ms,
         "permute_gbs": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9,
         "combine_gbs": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
+        "valid_rows_offsets_last": offsets_host[-1],
+        "predicted_mfma_flops": {"gemm_gate_up": pred_gu, "gemm_down": pred_dn},
         "roofline": {"kernel": "grouped_gemm gate/up + SiLU*up", "bound": "mfma",
                      "achieved": gu_tf, "peak": peak, "unit": "TFLOP/s", "frac": gu_tf / peak,
                      "traffic": traffic},
     }
+    if args.clamp_ab:
+        rec["clamp_ab"] = clamp_ab(g, cfg, inp, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(rec), flush=True)

@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     forward,
     forward_workspace_bytes,
     grouped_gemm,
+    grouped_gemm_tile_shape,
     permute,
     route_topk,
     unpermute_combine,

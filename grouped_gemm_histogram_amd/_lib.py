@@ -42,6 +42,8 @@ SIGNATURES: dict[str, tuple] = {
     "moe_build_offsets": (I32, [P, I64, I32, P, P, P, P, SZ, P]),
     "moe_permute": (I32, [P, I32, I64, I64, I32, P, P, I32, I64, P, I32, P, P]),
     "moe_grouped_gemm": (I32, [P, P, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P, P]),
+    "moe_grouped_gemm_tile_shape": (I32, [I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                          ctypes.POINTER(I32)]),
     "moe_unpermute_combine": (I32, [P, I32, P, P, P, I32, I64, I64, I32, P, I32, P]),
     "moe_forward_workspace": (SZ, [I64, I64, I64, I32, I32, I32]),
     "moe_forward": (I32, [P, I32, P, P, P, P, P, I32, I64, I64, I64, I32, I32, I64, I32, P, I32,
@@ -59,6 +61,7 @@ class MoeKernels:
     build_offsets: Callable
     permute: Callable
     grouped_gemm: Callable
+    grouped_gemm_tile_shape: Callable
     unpermute_combine: Callable
     forward_workspace: Callable
     forward: Callable

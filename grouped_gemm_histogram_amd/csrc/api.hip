@@ -210,6 +210,19 @@ moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* 
   return launched(moe::launch_grouped_gemm(p, as_stream(stream)), "grouped_gemm");
 }
 
+moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int32_t* tile_m,
+                                         int32_t* tile_n, int32_t* k_slice) {
+  MOE_REQUIRE(tile_m && tile_n && k_slice, "null output pointer");
+  MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
+  int m = 0, n = 0, ks = 0;
+  if (!moe::grouped_gemm_tile_shape(ab_dtype, epi == MOE_EPI_SILU_MUL, &m, &n, &ks))
+    return fail(MOE_ERR_INVALID_ARG, "bad dtype %d", (int)ab_dtype);
+  *tile_m = m;
+  *tile_n = n;
+  *k_slice = ks;
+  return ok();
+}
+
 moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int32_t* row_pos,
                                    const float* topk_weights, const int32_t* offsets, int32_t E,
                                    int64_t T, int64_t H, int32_t k, void* out,

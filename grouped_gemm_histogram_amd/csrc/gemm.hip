@@ -675,6 +675,36 @@ hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+template <int BM, int BNB, int WM, int WN, int PF, int ST>
+struct TileOf {
+  static constexpr int kM = BM, kN = BNB;
+};
+}  // namespace
+
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice) {
+  if (ab_dtype == 1) {
+    using T1 = TileOf<MOE_TILE_BF16_SILU>;
+    using T0 = TileOf<MOE_TILE_BF16_NONE>;
+    *tile_m = silu ? T1::kM : T0::kM;
+    *tile_n = silu ? T1::kN : T0::kN;
+    *k_slice = kSliceBytes / 2;
+  } else if (ab_dtype == 0) {
+    *tile_m = 64;
+    *tile_n = 64;
+    *k_slice = kSliceBytes / 4;
+  } else if (ab_dtype == 2) {
+    using T1 = TileOf<MOE_TILE_FP8_SILU>;
+    using T0 = TileOf<MOE_TILE_FP8_NONE>;
+    *tile_m = silu ? T1::kM : T0::kM;
+    *tile_n = silu ? T1::kN : T0::kN;
+    *k_slice = kSliceBytes;
+  } else {
+    return false;
+  }
+  return true;
+}
+
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   GemmArgs a{};
   a.A = static_cast<const uint8_t*>(p.A);

@@ -35,6 +35,7 @@ struct GemmLaunch {
   float* c_scales;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice);
 
 hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const float* weights,
                           const int* offsets, int E, int T, int H, int k, void* out, bool out_bf16,

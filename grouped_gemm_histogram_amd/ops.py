@@ -130,6 +130,14 @@ def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilog
     return (out, out_scales) if fp8_out else out
 
 
+def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str = "none"):
+    """(tile rows, tile weight rows, K elements per slice) of moe_grouped_gemm for a dtype/epilogue."""
+    m, n, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().grouped_gemm_tile_shape(_DT[dtype], _EPI[epilogue], ctypes.byref(m), ctypes.byref(n),
+                                          ctypes.byref(k)))
+    return m.value, n.value, k.value
+
+
 def unpermute_combine(y: torch.Tensor, row_pos: torch.Tensor, topk_weights: torch.Tensor,
                       offsets: torch.Tensor, k: int, out_dtype: Optional[torch.dtype] = None,
                       out: Optional[torch.Tensor] = None):

@@ -167,6 +167,18 @@ moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* 
                               void* stream);
 
 /*
+ * moe_grouped_gemm_tile_shape -- the tile moe_grouped_gemm uses for a dtype and
+ * epilogue: *tile_m activation rows by *tile_n weight rows (SiLU*up tiles
+ * hold tile_n/2 gate and tile_n/2 up rows), *k_slice elements of K per step.
+ * Lets a caller predict the MFMA work from offsets: each expert segment of
+ * M_e rows is covered by ceil(M_e / tile_m) tiles in M, each computing
+ * 16 * ceil(rows / 16) rows.  Returns MOE_ERR_INVALID_ARG for bad enums or
+ * null outputs.
+ */
+moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int32_t* tile_m,
+                                         int32_t* tile_n, int32_t* k_slice);
+
+/*
  * moe_unpermute_combine -- back to token order, scaled by the routing
  * weights (the gather step of [LF10481] section 1):
  *

@@ -48,6 +48,16 @@ def test_version_and_strings(lib):
     assert lib.status_string(3) == b"MOE_ERR_WORKSPACE"
 
 
+def test_tile_shape_query(lib):
+    m, n, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    for dt in (0, 1, 2):
+        for epi in (0, 1):
+            assert lib.grouped_gemm_tile_shape(dt, epi, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 0
+            assert m.value % 16 == 0 and n.value % 32 == 0 and k.value * (4, 2, 1)[dt] == 128
+    assert lib.grouped_gemm_tile_shape(7, 0, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
+    assert lib.grouped_gemm_tile_shape(1, 0, None, ctypes.byref(n), ctypes.byref(k)) == 1
+
+
 def test_host_validation(lib):
     INVALID, UNSUP, WS = 1, 2, 3
     assert lib.route_topk(None, 4, 0, 1, -1, 1, None, None, None) == INVALID
