@@ -90,10 +90,10 @@ constexpr int kMaxExperts = 1024;
 #define MOE_TILE_BF16_NONE 192, 192, 4, 2, 0, 3
 #endif
 #ifndef MOE_TILE_FP8_SILU
-#define MOE_TILE_FP8_SILU 128, 256, 2, 2, 1, 2
+#define MOE_TILE_FP8_SILU 128, 256, 4, 2, 0, 3
 #endif
 #ifndef MOE_TILE_FP8_NONE
-#define MOE_TILE_FP8_NONE 128, 128, 2, 2, 1, 2
+#define MOE_TILE_FP8_NONE 128, 256, 4, 2, 0, 3
 #endif
 
 // Swizzle of the 16-byte chunk index within a 128-byte LDS row: logical chunk c
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = (int)__builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: lives in an SGPR
   const int wm = wave % WM;
   const int wn = wave / WM;
   const int ii = lane & 15;   // MFMA row/column index of this lane
@@ -346,12 +346,36 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
       float afac[SM][2];
       if constexpr (AB == AbType::FP8) {
-        const float sb0 = bsc[nb_half[0] * KB + kt];
-        const float sb1 = bsc[nb_half[1] * KB + kt];
+        // Scales are read through the constant address space at wave-uniform
+        // addresses, i.e. with scalar loads (counted by lgkmcnt, not vmcnt), so
+        // they never make the compiler wait for the in-flight direct loads.
+        // Lane ii then picks the scale of its row from the subtile's 16.
+        typedef const __attribute__((address_space(4))) float* cfloat_p;
+        const cfloat_p bs = (cfloat_p)bsc;
+        const float sb0 = bs[uniform_u32((uint32_t)(nb_half[0] * KB + kt))];
+        const float sb1 = bs[uniform_u32((uint32_t)(nb_half[1] * KB + kt))];
+        // activation scales are block-major ([K/128, M_rows]): the 16 rows of a
+        // subtile are 16 consecutive floats of block kt, one 64-byte scalar load
+        // (the window slides back at the end of the buffer; lanes past the last
+        // row read a neighbour's scale, which only feeds rows that are not stored)
+        const cfloat_p as = (cfloat_p)(args.a_scales + (long long)kt * args.M_rows);
+        const int Mr = args.M_rows;
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
-          const int r = min(m0 + 16 * (t * WM + wm) + ii, seg_end - 1);
-          const float sa = args.a_scales[(long long)r * KB + kt];
+          const int r0 = (int)uniform_u32((uint32_t)(m0 + 16 * (t * WM + wm)));
+          float sa;
+          if (Mr >= 16) {
+            const int w0 = min(r0, Mr - 16);
+            const int sel = ii + (r0 - w0);
+            sa = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float si = as[w0 + i];
+              sa = (sel == i) ? si : sa;
+            }
+          } else {
+            sa = as[min(r0 + ii, Mr - 1)];
+          }
           afac[t][0] = sa * sb0;
           afac[t][1] = sa * sb1;
         }
@@ -388,6 +412,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
                                     af[t][c].w & keep);
           }
         }
+        // fp8: each 128-deep MFMA yields one block's partial sums; all of the
+        // slice's partials are issued before any is scaled, so the scale FMAs
+        // never wait on the MFMA just issued.
+        f32x4 part[AB == AbType::FP8 ? SM : 1][AB == AbType::FP8 ? SNB : 1];
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
           if (t > 0 || step > 0) hook(step * SM + t - 1);   // between rows of MFMAs
@@ -410,11 +438,20 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
                                 (int)wf[s][1].x, (int)wf[s][1].y, (int)wf[s][1].z, (int)wf[s][1].w};
               const i32x8 av = {(int)af[t][0].x, (int)af[t][0].y, (int)af[t][0].z, (int)af[t][0].w,
                                 (int)af[t][1].x, (int)af[t][1].y, (int)af[t][1].z, (int)af[t][1].w};
-              const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              part[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   wv, av, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            }
+          }
+        }
+        if constexpr (AB == AbType::FP8) {
+#pragma unroll
+          for (int t = 0; t < SM; ++t) {
+            if (!live[t]) continue;
+#pragma unroll
+            for (int s = 0; s < SNB; ++s) {
               const float f = afac[t][SILU ? (s / SNO) : 0];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(part[r], f, acc[t][s][r]);
+              for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(part[t][s][r], f, acc[t][s][r]);
             }
           }
         }
@@ -471,6 +508,108 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         };
         const bool has_tail = (k_bytes % kSliceBytes) != 0;
         int st = gk % ST;                       // stage of slice kt
+        if constexpr (AB == AbType::BF16) {
+          // Software pipeline over the two 32-deep MFMA steps of a slice.  Step s+1's
+          // fragments are read into the other register set while step s's MFMAs
+          // issue, and the slice barrier sits between the two steps, so that the
+          // MFMAs of step 1 (operands already in registers) cover the LDS reads of
+          // the next slice's step 0 instead of the whole workgroup stalling on them.
+          //
+          // Stage reuse: the loads of slice kt+2 land in the stage of slice kt-1.
+          // Every wave has finished reading slice kt-1 before barrier kt-1 (its reads
+          // are drained with lgkmcnt(0) there), and slice kt+2's loads are issued
+          // after it, in the body of slice kt.
+          static_assert(ST == 3, "the pipelined loop needs three LDS stages");
+          constexpr bool FULL = decltype(full_tag)::value;
+          bool live[SM];
+#pragma unroll
+          for (int t = 0; t < SM; ++t) live[t] = FULL || 16 * (t * WM + wm) < rows_valid;
+          auto read_step = [&](int stage, int step, uint4(&fa)[SM], uint4(&fw)[SNB]) MOE_INLINE {
+            const uint8_t* sA = smem[stage];
+            const uint8_t* sB = smem[stage] + BM * kSliceBytes;
+            const int coff = ((step * 4 + g) ^ rd_swz) << 4;
+#pragma unroll
+            for (int s = 0; s < SNB; ++s) {
+              int wrow;
+              if constexpr (SILU) {
+                const int half = s / SNO, ss = s - half * SNO;
+                wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
+              } else {
+                wrow = wn * Cfg::kWNB + 16 * s + ii;
+              }
+              fw[s] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
+            }
+            // every subtile is read (its LDS rows always exist); dead ones skip only
+            // their MFMAs, so the reads need no exec mask
+#pragma unroll
+            for (int t = 0; t < SM; ++t)
+              fa[t] = *reinterpret_cast<const uint4*>(sA + (16 * (t * WM + wm) + ii) * kSliceBytes + coff);
+          };
+          // keep: all-ones, or zero for a K chunk past the end (its bytes are copies
+          // of the row's last chunk); zeroing the activation side suffices
+          auto mma_row = [&](int t, const uint4(&fa)[SM], const uint4(&fw)[SNB], uint32_t keep) MOE_INLINE {
+            if (!live[t]) return;
+            const uint4 a = make_uint4(fa[t].x & keep, fa[t].y & keep, fa[t].z & keep, fa[t].w & keep);
+#pragma unroll
+            for (int s = 0; s < SNB; ++s)
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[s]),
+                                                                  __builtin_bit_cast(bf16x8, a), acc[t][s], 0, 0, 0);
+          };
+          uint4 fa0[SM], fw0[SNB], fa1[SM], fw1[SNB];
+          issue(0, st);
+          if (KT > 1) {
+            issue(1, st == 2 ? 0 : st + 1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
+          } else {
+            wait_all_vm();
+          }
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          read_step(st, 0, fa0, fw0);
+          // one slice; LAST = no next slice (no barrier, no reads of it).  The last
+          // slice is peeled off so that the body is straight-line code and the
+          // compiler's LDS wait counts stay exact.
+          auto body = [&](int kt, auto last_tag) MOE_INLINE {
+            constexpr bool LAST = decltype(last_tag)::value;
+            const bool tail = LAST && has_tail;
+            const uint32_t keep0 = (tail && kt * kSliceBytes + g * 16 >= k_bytes) ? 0u : ~0u;
+            const uint32_t keep1 = (tail && kt * kSliceBytes + (4 + g) * 16 >= k_bytes) ? 0u : ~0u;
+            read_step(st, 1, fa1, fw1);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool more = kt + 2 < KT;
+            const int st2 = (st == 0) ? 2 : st - 1;   // stage of slice kt+2
+#pragma unroll
+            for (int t = 0; t < SM; ++t) {
+              mma_row(t, fa0, fw0, keep0);
+              if (!LAST && more) {
+#pragma unroll
+                for (int j = 0; j < Cfg::kDmaPerSlice; ++j)
+                  if (j * SM / Cfg::kDmaPerSlice == t) issue_one(j, kt + 2, st2);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            const int st1 = (st == 2) ? 0 : st + 1;
+            if constexpr (!LAST) {
+              // slice kt+1 has landed once only slice kt+2's loads are outstanding
+              if (more)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
+              else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+              __builtin_amdgcn_s_barrier();
+              asm volatile("" ::: "memory");
+              read_step(st1, 0, fa0, fw0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int t = 0; t < SM; ++t) mma_row(t, fa1, fw1, keep1);
+            __builtin_amdgcn_sched_barrier(0);
+            st = st1;
+          };
+          for (int kt = 0; kt + 1 < KT; ++kt) body(kt, std::integral_constant<bool, false>{});
+          body(KT - 1, std::integral_constant<bool, true>{});
+          gk += KT;
+          return;
+        }
         issue(0, st);
         if constexpr (ST == 3) {
           if (KT > 1) issue(1, st == 2 ? 0 : st + 1);
@@ -579,7 +718,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           uint8_t* dst = args.C + m * N_out + cbase;
           static_assert(SNO == 4, "fp8 epilogue writes 16 codes per lane");
           *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-          if (wn == 0 && g == 0) args.c_scales[m * (N_out / 128) + n0 / 128] = scale;
+          if (wn == 0 && g == 0) args.c_scales[(long long)(n0 / 128) * args.M_rows + m] = scale;
         }
       } else if constexpr (CT == CType::BF16) {
         if (row_ok) {
@@ -630,10 +769,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       for (long long i = (long long)blockIdx.x * THREADS + tid; i < n16; i += (long long)G * THREADS)
         base[i] = make_uint4(0, 0, 0, 0);
       if constexpr (CT == CType::FP8) {
+        // block-major scales [N_out/128, M_rows]: rows [V, M_rows) of every block
         const long long ns = rows * (N_out / 128);
-        float* sb = args.c_scales + V * (N_out / 128);
         for (long long i = (long long)blockIdx.x * THREADS + tid; i < ns; i += (long long)G * THREADS)
-          sb[i] = 1.0f;
+          args.c_scales[(i / rows) * args.M_rows + V + (i % rows)] = 1.0f;
       }
     }
   }

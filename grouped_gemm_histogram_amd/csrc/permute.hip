@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   for (; c < n16; c += kWave) d[c] = s[c];
 }
 
-// bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [R, H/128]; H % 128 == 0.
+// bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [H/128, R]; H % 128 == 0.
 // Each 16-lane group of the wave owns one 128-channel group per step.
 __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restrict__ x, int T,
                                                             int H, int k, const int* __restrict__ sorted_rows,
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restr
   const int n8 = H / 8;                       // 8-channel units per row
   const uint4* s = x + (size_t)src * n8;
   uint2* d = xq + (size_t)p * n8;
-  float* sc = xs + (size_t)p * (H / 128);
+  float* sc = xs + p;                         // scales are block-major: [H/128, R]
   for (int base = 0; base < n8; base += kWave) {
     const int u = base + lane;
     const bool active = u < n8;               // whole 16-lane groups, as H % 128 == 0
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restr
       hi = cvt_e4m3x2(clamp448(v[4] / scale), clamp448(v[5] / scale)) |
            (cvt_e4m3x2(clamp448(v[6] / scale), clamp448(v[7] / scale)) << 16);
       d[u] = make_uint2(lo, hi);
-      if ((lane & 15) == 0) sc[u / 16] = scale;
+      if ((lane & 15) == 0) sc[(size_t)(u / 16) * R] = scale;
     }
   }
 }

@@ -80,7 +80,7 @@ def build_offsets(topk_ids: torch.Tensor, E: int):
 def permute(x: torch.Tensor, sorted_rows: torch.Tensor, offsets: torch.Tensor, k: int,
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
             out_scales: Optional[torch.Tensor] = None):
-    """x [T, H] -> x_perm [R, H] (rows >= offsets[E] untouched); fp8 also returns scales [R, H/128]."""
+    """x [T, H] -> x_perm [R, H] (rows >= offsets[E] untouched); fp8 also returns scales [H/128, R]."""
     _need(x, "x", (torch.float32, torch.bfloat16))
     T, H = x.shape
     R = sorted_rows.numel()
@@ -93,7 +93,7 @@ def permute(x: torch.Tensor, sorted_rows: torch.Tensor, offsets: torch.Tensor, k
     _need(out, "out", out_dtype, (R, H), x.device)
     fp8 = out_dtype == torch.float8_e4m3fn
     if fp8 and out_scales is None:
-        out_scales = torch.empty(R, H // 128, dtype=torch.float32, device=x.device)
+        out_scales = torch.empty(H // 128, R, dtype=torch.float32, device=x.device)
     _check(load().permute(_p(x), _DT[x.dtype], T, H, k, _p(sorted_rows), _p(offsets), E, R,
                           _p(out), _DT[out_dtype], _p(out_scales) if fp8 else None, _stream(x)))
     return (out, out_scales) if fp8 else out
@@ -103,7 +103,11 @@ def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilog
                  a_scales: Optional[torch.Tensor] = None, b_scales: Optional[torch.Tensor] = None,
                  out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None):
-    """a [M, K] x b [E, N, K] over segments of offsets -> c [M, N or N/2] (+ scales for fp8 out)."""
+    """a [M, K] x b [E, N, K] over segments of offsets -> c [M, N or N/2] (+ scales for fp8 out).
+
+    fp8 activation scales (a_scales, and the returned scales) are block-major:
+    [K/128, M] and [N_out/128, M].
+    """
     _need(a, "a", tuple(_DT))
     M, K = a.shape
     E, N, K2 = b.shape
@@ -113,7 +117,7 @@ def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilog
     _need(offsets, "offsets", torch.int32, (E + 1,), a.device)
     fp8 = a.dtype == torch.float8_e4m3fn
     if fp8:
-        _need(a_scales, "a_scales", torch.float32, (M, K // 128), a.device)
+        _need(a_scales, "a_scales", torch.float32, (K // 128, M), a.device)
         _need(b_scales, "b_scales", torch.float32, (E, N // 128, K // 128), a.device)
     n_out = N // 2 if epilogue == "silu_mul" else N
     out_dtype = out_dtype or (torch.bfloat16 if fp8 else a.dtype)
@@ -122,7 +126,7 @@ def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilog
     _need(out, "out", out_dtype, (M, n_out), a.device)
     fp8_out = out_dtype == torch.float8_e4m3fn
     if fp8_out and out_scales is None:
-        out_scales = torch.empty(M, n_out // 128, dtype=torch.float32, device=a.device)
+        out_scales = torch.empty(n_out // 128, M, dtype=torch.float32, device=a.device)
     _check(load().grouped_gemm(_p(a), _p(a_scales) if fp8 else None, _p(b),
                                _p(b_scales) if fp8 else None, _DT[a.dtype], _p(offsets), E, M, N, K,
                                _EPI[epilogue], _p(out), _DT[out_dtype],

@@ -32,8 +32,9 @@
  *    with K contiguous.
  *  - fp8 is OCP E4M3 ("e4m3fn", max 448).  fp8 weights carry one fp32 scale
  *    per 128x128 block ([E, N/128, K/128]); fp8 activations carry one fp32
- *    scale per row and 128 consecutive channels ([rows, K/128]).  A value is
- *    code * scale.  Activation scales are amax/448 (1 for an all-zero group),
+ *    scale per row and 128 consecutive channels, stored channel-block-major
+ *    ([K/128, rows]: the scales of one 128-channel block are contiguous over
+ *    rows).  A value is code * scale.  Activation scales are amax/448 (1 for an all-zero group),
  *    codes are round-to-nearest-even of value/scale, saturating.
  *  - Every call validates its arguments on the host first and returns
  *    MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE without
@@ -126,7 +127,7 @@ moe_status_t moe_build_offsets(const int32_t* topk_ids, int64_t R, int32_t E,
  *                H % 128 == 0): each row is quantised per 128 channels
  *                (the per-token activation cast that [T45621] section 1
  *                loads as fp8_act_quant / per_token_cast_to_fp8) into
- *                x_perm codes [R, H] and x_perm_scales f32 [R, H/128].
+ *                x_perm codes [R, H] and x_perm_scales f32 [H/128, R].
  *   R            rows of x_perm (>= offsets[E]); T*k for the layer.
  */
 moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t H, int32_t k,
@@ -141,7 +142,7 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t 
  *
  *   for p in [offsets[e], offsets[e+1]):  acc[p, n] = sum_k A[p, k] * B[e, n, k]
  *
- *   A         [M_rows, K] of ab_dtype; a_scales f32 [M_rows, K/128] for fp8.
+ *   A         [M_rows, K] of ab_dtype; a_scales f32 [K/128, M_rows] for fp8.
  *   B         [E, N, K] of ab_dtype;   b_scales f32 [E, N/128, K/128] for fp8.
  *   ab_dtype  MOE_F32, MOE_BF16 or MOE_FP8_E4M3 (K % 128 == 0 for fp8).
  *   offsets   device int32 [E+1]; read on the device (no host sync).
@@ -152,7 +153,7 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t 
  *   C         [M_rows, N_out] of c_dtype: MOE_F32, MOE_BF16, or MOE_FP8_E4M3
  *             (ab_dtype fp8 and N_out % 128 == 0: rows quantised per 128
  *             channels from the fp32 result, scales in c_scales
- *             f32 [M_rows, N_out/128]).
+ *             f32 [N_out/128, M_rows]).
  *
  * Only rows below offsets[E] are computed: no tile is launched past the last
  * valid row.  Rows [offsets[E], M_rows) of C are written as exact zeros

@@ -175,7 +175,7 @@ def test_permute_quant_fp8(case):
     rq = olayer.permute_rows(xq, sr, off, k)
     rs = olayer.permute_rows(xs, sr, off, k)
     gq = npu8(q)[:V]
-    gs = s.cpu().numpy()[:V]
+    gs = np.ascontiguousarray(s.cpu().numpy().T[:V])   # block-major [H/128, R] -> [R, H/128]
     bad = np.argwhere(gq != rq)
     assert bad.size == 0, (bad[:5], gq[tuple(bad[0])], rq[tuple(bad[0])])
     assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
@@ -292,11 +292,11 @@ def test_grouped_gemm_fp8(M, V, E, N, K, epi, out):
     n_out = N // 2 if epi == "silu_mul" else N
     C = torch.full((M, n_out), float("nan"), dtype=torch.float32, device=DEV).to(odt)
     res = g.grouped_gemm(_u8_to_fp8(aq), _u8_to_fp8(bq), torch.from_numpy(off).to(DEV), epi,
-                         a_scales=torch.from_numpy(as_).to(DEV), b_scales=torch.from_numpy(bs).to(DEV),
-                         out_dtype=odt, out=C)
+                         a_scales=torch.from_numpy(np.ascontiguousarray(as_.T)).to(DEV),
+                         b_scales=torch.from_numpy(bs).to(DEV), out_dtype=odt, out=C)
     if out == "fp8":
         C, Cs = res
-        gq, gs = npu8(C), Cs.cpu().numpy()
+        gq, gs = npu8(C), Cs.cpu().numpy().T   # block-major -> [M, N_out/128]
         rd, rq, rs = ogemm.grouped_gemm(aq, bq, off, epi, as_, bs, out_fp8=True)
         assert np.all(gq[V:] == 0) and np.all(gs[V:] == 1.0)
         if V:
@@ -332,8 +332,8 @@ def test_grouped_gemm_fp8_exact():
     off = _segments(M, E, 380, 22)
     g = ops()
     C = g.grouped_gemm(_u8_to_fp8(aq), _u8_to_fp8(bq), torch.from_numpy(off).to(DEV), "none",
-                       a_scales=torch.from_numpy(as_).to(DEV), b_scales=torch.from_numpy(bs).to(DEV),
-                       out_dtype=torch.float32)
+                       a_scales=torch.from_numpy(np.ascontiguousarray(as_.T)).to(DEV),
+                       b_scales=torch.from_numpy(bs).to(DEV), out_dtype=torch.float32)
     ref = ogemm.grouped_gemm(aq, bq, off, "none", as_, bs)
     assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
 
