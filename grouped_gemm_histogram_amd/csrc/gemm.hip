@@ -90,10 +90,10 @@ constexpr int kMaxExperts = 1024;
 #define MOE_TILE_BF16_NONE 192, 192, 4, 2, 0, 3
 #endif
 #ifndef MOE_TILE_FP8_SILU
-#define MOE_TILE_FP8_SILU 128, 256, 4, 2, 0, 3
+#define MOE_TILE_FP8_SILU 128, 256, 2, 4, 0, 3
 #endif
 #ifndef MOE_TILE_FP8_NONE
-#define MOE_TILE_FP8_NONE 128, 256, 4, 2, 0, 3
+#define MOE_TILE_FP8_NONE 128, 256, 2, 4, 0, 3
 #endif
 
 // Swizzle of the 16-byte chunk index within a 128-byte LDS row: logical chunk c
@@ -111,6 +111,14 @@ __device__ __forceinline__ int swz(int row) { return row & 7; }
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+// Same with 4 bytes per lane (global_load_lds_dword): lane i's word lands at
+// lds_addr + 4*i.
+__device__ __forceinline__ void dma4(uint32_t lds_addr, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(lds_addr), "v"(voff), "s"(base)
                : "memory", "m0");
@@ -158,6 +166,18 @@ struct GemmCfg {
   static_assert(ST == 2 || (PF == 0 && ST == 3), "LDS stages: 2, or 3 with direct loads");
   static constexpr int kDmaPerSlice = kDmaA + kDmaB;
   static_assert(CT != CType::FP8 || (SILU && kBNOut == 128), "fp8 output needs 128-column tiles");
+  // fp8 runs on direct loads only.  Each LDS stage then also holds the slice's
+  // block scales: one 256-byte area per wave, filled by one 4-byte-per-lane direct
+  // load per wave (waves [0, BM/64): the tile rows' activation scales; the other
+  // waves: the weight scales, read from the first of them).
+  static_assert(AB != AbType::FP8 || PF == 0, "fp8 needs direct loads");
+  static constexpr bool kLdsScales = AB == AbType::FP8;
+  static constexpr int kScaleWaves = BM / 64;
+  static_assert(!kLdsScales || (BM % 64 == 0 && kScaleWaves < kNW && 2 * WN <= 64),
+                "fp8 tiles: BM a multiple of 64 and a spare wave for the weight scales");
+  static constexpr int kScaleBytes = kLdsScales ? kNW * 256 : 0;
+  static constexpr int kStageBytes = kTileBytes + kScaleBytes;
+  static constexpr int kDmaTotal = kDmaPerSlice + (kLdsScales ? 1 : 0);   // loads per wave per slice
 };
 
 // Output column (within the wave's slab) held by MFMA row ii of subtile s.
@@ -173,7 +193,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   constexpr int THREADS = Cfg::kThreads;
   constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[ST][Cfg::kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST][Cfg::kStageBytes];
   __shared__ int s_mt_pre[kMaxExperts + 1];
   __shared__ float s_red[(CT == CType::FP8) ? WN * BM : 1];
 
@@ -315,28 +335,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
       for (int s = 0; s < SNB; ++s) acc[t][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // fp8: weight block-scale rows of this wave (gate / up halves, or the single slab)
-    const float* bsc = nullptr;
-    int nb_half[2] = {0, 0};
-    const int KB = K / 128;
-    if constexpr (AB == AbType::FP8) {
-      const int NB = args.N / 128;
-      if constexpr (SILU) {
-        nb_half[0] = (n0 + wn * Cfg::kWNOut) / 128;
-        nb_half[1] = (N_out + n0 + wn * Cfg::kWNOut) / 128;
-      } else {
-        nb_half[0] = nb_half[1] = (n0 + wn * Cfg::kWNB) / 128;
-      }
-      nb_half[0] = min(nb_half[0], NB - 1);
-      nb_half[1] = min(nb_half[1], NB - 1);
-      bsc = args.b_scales + (long long)e * NB * KB;
-    }
-
     // Activation subtile t of wave wm holds tile rows 16*(t*WM + wm) + [0, 16): the
     // waves of a column interleave, so a short tile still spreads over all of them.
     // FULL = every subtile has valid rows; otherwise subtiles past rows_valid skip
     // their LDS reads and MFMAs.
-    auto compute = [&](auto full_tag, int buf, int kt, bool k_tail, auto&& hook) MOE_INLINE {
+    // Register-prefetch path (bf16 and f32): per slice, all fragments of a step are
+    // read, then that step's MFMAs issue.
+    auto compute = [&](auto full_tag, int buf, int kt, bool k_tail) MOE_INLINE {
+      static_assert(AB != AbType::FP8, "fp8 runs on direct loads");
       constexpr bool FULL = decltype(full_tag)::value;
       const uint8_t* sA = smem[buf];
       const uint8_t* sB = smem[buf] + BM * kSliceBytes;
@@ -344,119 +350,50 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
       for (int t = 0; t < SM; ++t) live[t] = FULL || 16 * (t * WM + wm) < rows_valid;
 
-      float afac[SM][2];
-      if constexpr (AB == AbType::FP8) {
-        // Scales are read through the constant address space at wave-uniform
-        // addresses, i.e. with scalar loads (counted by lgkmcnt, not vmcnt), so
-        // they never make the compiler wait for the in-flight direct loads.
-        // Lane ii then picks the scale of its row from the subtile's 16.
-        typedef const __attribute__((address_space(4))) float* cfloat_p;
-        const cfloat_p bs = (cfloat_p)bsc;
-        const float sb0 = bs[uniform_u32((uint32_t)(nb_half[0] * KB + kt))];
-        const float sb1 = bs[uniform_u32((uint32_t)(nb_half[1] * KB + kt))];
-        // activation scales are block-major ([K/128, M_rows]): the 16 rows of a
-        // subtile are 16 consecutive floats of block kt, one 64-byte scalar load
-        // (the window slides back at the end of the buffer; lanes past the last
-        // row read a neighbour's scale, which only feeds rows that are not stored)
-        const cfloat_p as = (cfloat_p)(args.a_scales + (long long)kt * args.M_rows);
-        const int Mr = args.M_rows;
-#pragma unroll
-        for (int t = 0; t < SM; ++t) {
-          const int r0 = (int)uniform_u32((uint32_t)(m0 + 16 * (t * WM + wm)));
-          float sa;
-          if (Mr >= 16) {
-            const int w0 = min(r0, Mr - 16);
-            const int sel = ii + (r0 - w0);
-            sa = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float si = as[w0 + i];
-              sa = (sel == i) ? si : sa;
-            }
-          } else {
-            sa = as[min(r0 + ii, Mr - 1)];
-          }
-          afac[t][0] = sa * sb0;
-          afac[t][1] = sa * sb1;
-        }
-      }
-
 #pragma unroll
       for (int step = 0; step < Tr::kSteps; ++step) {
-        uint4 af[SM][Tr::kChunksPerLane], wf[SNB][Tr::kChunksPerLane];
+        uint4 af[SM], wf[SNB];
+        const int ch = step * 4 + g;
+        const int coff = (ch ^ rd_swz) << 4;
 #pragma unroll
-        for (int c = 0; c < Tr::kChunksPerLane; ++c) {
-          const int ch = (Tr::kChunksPerLane == 1) ? (step * 4 + g) : (2 * g + c);
-          const int coff = (ch ^ rd_swz) << 4;
-#pragma unroll
-          for (int s = 0; s < SNB; ++s) {
-            int wrow;
-            if constexpr (SILU) {
-              const int half = s / SNO, ss = s - half * SNO;
-              wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
-            } else {
-              wrow = wn * Cfg::kWNB + 16 * s + ii;
-            }
-            wf[s][c] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
+        for (int s = 0; s < SNB; ++s) {
+          int wrow;
+          if constexpr (SILU) {
+            const int half = s / SNO, ss = s - half * SNO;
+            wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
+          } else {
+            wrow = wn * Cfg::kWNB + 16 * s + ii;
           }
-#pragma unroll
-          for (int t = 0; t < SM; ++t)
-            if (live[t])
-              af[t][c] = *reinterpret_cast<const uint4*>(sA + (16 * (t * WM + wm) + ii) * kSliceBytes + coff);
-          if (k_tail) {
-            // chunks past K hold copies of the row's last chunk: zero the activation side
-            const uint32_t keep = (kt * kSliceBytes + ch * 16 < k_bytes) ? 0xffffffffu : 0u;
-#pragma unroll
-            for (int t = 0; t < SM; ++t)
-              af[t][c] = make_uint4(af[t][c].x & keep, af[t][c].y & keep, af[t][c].z & keep,
-                                    af[t][c].w & keep);
-          }
+          wf[s] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
         }
-        // fp8: each 128-deep MFMA yields one block's partial sums; all of the
-        // slice's partials are issued before any is scaled, so the scale FMAs
-        // never wait on the MFMA just issued.
-        f32x4 part[AB == AbType::FP8 ? SM : 1][AB == AbType::FP8 ? SNB : 1];
+#pragma unroll
+        for (int t = 0; t < SM; ++t)
+          if (live[t]) af[t] = *reinterpret_cast<const uint4*>(sA + (16 * (t * WM + wm) + ii) * kSliceBytes + coff);
+        if (k_tail) {
+          // chunks past K hold copies of the row's last chunk: zero the activation side
+          const uint32_t keep = (kt * kSliceBytes + ch * 16 < k_bytes) ? 0xffffffffu : 0u;
+#pragma unroll
+          for (int t = 0; t < SM; ++t) af[t] = make_uint4(af[t].x & keep, af[t].y & keep, af[t].z & keep, af[t].w & keep);
+        }
 #pragma unroll
         for (int t = 0; t < SM; ++t) {
-          if (t > 0 || step > 0) hook(step * SM + t - 1);   // between rows of MFMAs
           if (!live[t]) continue;
 #pragma unroll
           for (int s = 0; s < SNB; ++s) {
             if constexpr (AB == AbType::BF16) {
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, wf[s][0]), __builtin_bit_cast(bf16x8, af[t][0]),
-                  acc[t][s], 0, 0, 0);
-            } else if constexpr (AB == AbType::F32) {
-              const float4 w4 = __builtin_bit_cast(float4, wf[s][0]);
-              const float4 a4 = __builtin_bit_cast(float4, af[t][0]);
+                  __builtin_bit_cast(bf16x8, wf[s]), __builtin_bit_cast(bf16x8, af[t]), acc[t][s], 0, 0, 0);
+            } else {
+              const float4 w4 = __builtin_bit_cast(float4, wf[s]);
+              const float4 a4 = __builtin_bit_cast(float4, af[t]);
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.x, a4.x, acc[t][s], 0, 0, 0);
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.y, a4.y, acc[t][s], 0, 0, 0);
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.z, a4.z, acc[t][s], 0, 0, 0);
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(w4.w, a4.w, acc[t][s], 0, 0, 0);
-            } else {
-              const i32x8 wv = {(int)wf[s][0].x, (int)wf[s][0].y, (int)wf[s][0].z, (int)wf[s][0].w,
-                                (int)wf[s][1].x, (int)wf[s][1].y, (int)wf[s][1].z, (int)wf[s][1].w};
-              const i32x8 av = {(int)af[t][0].x, (int)af[t][0].y, (int)af[t][0].z, (int)af[t][0].w,
-                                (int)af[t][1].x, (int)af[t][1].y, (int)af[t][1].z, (int)af[t][1].w};
-              part[t][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  wv, av, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            }
-          }
-        }
-        if constexpr (AB == AbType::FP8) {
-#pragma unroll
-          for (int t = 0; t < SM; ++t) {
-            if (!live[t]) continue;
-#pragma unroll
-            for (int s = 0; s < SNB; ++s) {
-              const float f = afac[t][SILU ? (s / SNO) : 0];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[t][s][r] = fmaf(part[t][s][r], f, acc[t][s][r]);
             }
           }
         }
       }
-      hook(Tr::kSteps * SM - 1);
     };
 
     // ---- K loop: LDS double buffer fed from registers, PF slices of loads in flight
@@ -492,19 +429,45 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           const int col = min(n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
           rowB[j] = (uint32_t)(half * N_out + col) * (uint32_t)k_bytes;
         }
-        // load j of this wave for slice kt (j < kDmaA: activation rows, else weight rows)
+        // fp8 block scales of slice kt: the activation-scale waves load the scales of
+        // tile rows wave*64 + lane (block-major layout: row-contiguous per K block;
+        // rows past the buffer repeat its last row), the others the weight scales
+        // of (wave column q/2, half q%2) in lane q < 2*WN (other lanes repeat lane 0)
+        const uint8_t* sc_u = nullptr;
+        uint32_t sc_off = 0, sc_step = 0;
+        if constexpr (Cfg::kLdsScales) {
+          if (wave < Cfg::kScaleWaves) {
+            const int r = min(m0 + wave * 64 + lane, args.M_rows - 1);
+            sc_u = uniform_ptr(reinterpret_cast<const uint8_t*>(args.a_scales));
+            sc_off = (uint32_t)r * 4u;
+            sc_step = (uint32_t)args.M_rows * 4u;
+          } else {
+            const int q = lane < 2 * WN ? lane : 0;
+            const int wq = q >> 1, hq = q & 1;
+            const int NB = args.N / 128;
+            int nb = SILU ? (hq * N_out + n0 + wq * Cfg::kWNOut) / 128 : (n0 + wq * Cfg::kWNB) / 128;
+            nb = min(nb, NB - 1);
+            sc_u = uniform_ptr(reinterpret_cast<const uint8_t*>(args.b_scales + (long long)e * NB * (K / 128)));
+            sc_off = (uint32_t)(nb * (K / 128)) * 4u;
+            sc_step = 4u;
+          }
+        }
+        // load j of this wave for slice kt (j < kDmaA: activation rows; < kDmaPerSlice:
+        // weight rows; fp8: then the block scales)
         auto issue_one = [&](int j, int kt, int stage) MOE_INLINE {
           const uint32_t o = min((uint32_t)(kt * kSliceBytes) + cc, (uint32_t)(k_bytes - 16));
-          const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kTileBytes;
+          const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kStageBytes;
           if (j < Cfg::kDmaA)
             dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + o);
-          else
+          else if (j < Cfg::kDmaPerSlice)
             dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + (j - Cfg::kDmaA)) * 1024u, b_u,
                   rowB[j - Cfg::kDmaA] + o);
+          else
+            dma4(sb + Cfg::kTileBytes + wave_u * 256u, sc_u, sc_off + (uint32_t)kt * sc_step);
         };
         auto issue = [&](int kt, int stage) MOE_INLINE {
 #pragma unroll
-          for (int j = 0; j < Cfg::kDmaPerSlice; ++j) issue_one(j, kt, stage);
+          for (int j = 0; j < Cfg::kDmaTotal; ++j) issue_one(j, kt, stage);
         };
         const bool has_tail = (k_bytes % kSliceBytes) != 0;
         int st = gk % ST;                       // stage of slice kt
@@ -608,72 +571,176 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           for (int kt = 0; kt + 1 < KT; ++kt) body(kt, std::integral_constant<bool, false>{});
           body(KT - 1, std::integral_constant<bool, true>{});
           gk += KT;
-          return;
-        }
-        issue(0, st);
-        if constexpr (ST == 3) {
-          if (KT > 1) issue(1, st == 2 ? 0 : st + 1);
-        }
-        for (int kt = 0; kt < KT; ++kt) {
-          // slice kt has landed once at most the loads of later slices are outstanding
-          if constexpr (ST == 3) {
-            if (kt + 1 < KT)
-              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
-            else
-              wait_all_vm();
+        } else {
+          static_assert(AB == AbType::FP8, "direct loads serve bf16 and fp8");
+          // Software pipeline over the two column halves of a slice (the slice's K is
+          // one 128-deep MFMA).  The second half's weight fragments are read while the
+          // first half's MFMAs issue, and the slice barrier sits between the halves,
+          // so that the second half's MFMAs cover the reads of the next slice's
+          // activations, first-half weights and block scales.  Stage reuse as in the
+          // bf16 loop: slice kt+2's loads go to the stage of slice kt-1 and are issued
+          // after barrier kt-1.  Each 128-deep MFMA gives one K block's partial sums,
+          // which are scaled by (activation scale x weight scale) into the accumulator.
+          static_assert(ST == 3, "the pipelined loop needs three LDS stages");
+          static_assert(SNB % 2 == 0, "two column halves");
+          constexpr int SH = SNB / 2;   // weight subtiles per half (SiLU: gate, then up)
+          constexpr bool FULL = decltype(full_tag)::value;
+          bool live[SM];
+#pragma unroll
+          for (int t = 0; t < SM; ++t) live[t] = FULL || 16 * (t * WM + wm) < rows_valid;
+          // fragments are kept as the MFMA's 8-register operands (two 16-byte reads each)
+          struct ASet {
+            i32x8 a[SM];
+            float sa[SM];
+            float sb[2];
+          };
+          auto ld32 = [](const uint8_t* base, int row, int c0) MOE_INLINE {
+            const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kSliceBytes + (((c0) ^ swz(row)) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kSliceBytes + (((c0 + 1) ^ swz(row)) << 4));
+            return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          };
+          auto read_a = [&](int stage, ASet& x) MOE_INLINE {
+            const uint8_t* sA = smem[stage];
+            const uint8_t* scs = smem[stage] + Cfg::kTileBytes;
+#pragma unroll
+            for (int t = 0; t < SM; ++t) {
+              const int row = 16 * (t * WM + wm) + ii;
+              x.a[t] = ld32(sA, row, 2 * g);
+              x.sa[t] = *reinterpret_cast<const float*>(scs + row * 4);
+            }
+            x.sb[0] = *reinterpret_cast<const float*>(scs + Cfg::kScaleWaves * 256 + (2 * wn) * 4);
+            x.sb[1] = *reinterpret_cast<const float*>(scs + Cfg::kScaleWaves * 256 + (2 * wn + 1) * 4);
+          };
+          auto read_w = [&](int stage, int h, i32x8(&w)[SH]) MOE_INLINE {
+            const uint8_t* sB = smem[stage] + BM * kSliceBytes;
+#pragma unroll
+            for (int sl = 0; sl < SH; ++sl) {
+              const int sidx = h * SH + sl;
+              int wrow;
+              if constexpr (SILU) {
+                const int half = sidx / SNO, ss = sidx - half * SNO;
+                wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
+              } else {
+                wrow = wn * Cfg::kWNB + 16 * sidx + ii;
+              }
+              w[sl] = ld32(sB, wrow, 2 * g);
+            }
+          };
+          // within a row, partial sums are scaled one MFMA behind, so no FMA waits on
+          // the MFMA just issued
+          auto mma_half = [&](int h, const ASet& x, const i32x8(&w)[SH], auto&& dma_row) MOE_INLINE {
+#pragma unroll
+            for (int t = 0; t < SM; ++t) {
+              dma_row(t);
+              if (!live[t]) continue;
+              const float f = x.sa[t] * x.sb[h];
+              f32x4 prev;
+#pragma unroll
+              for (int sl = 0; sl < SH; ++sl) {
+                const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    w[sl], x.a[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if (sl > 0) {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) acc[t][h * SH + sl - 1][r] = fmaf(prev[r], f, acc[t][h * SH + sl - 1][r]);
+                }
+                prev = cur;
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[t][h * SH + SH - 1][r] = fmaf(prev[r], f, acc[t][h * SH + SH - 1][r]);
+            }
+          };
+          auto next_stage = [](int x) MOE_INLINE { return (x + 1 == ST) ? 0 : x + 1; };
+          ASet A0, A1;
+          i32x8 w0[SH], w1[SH];
+          issue(0, st);
+          if (KT > 1) {
+            issue(1, next_stage(st));
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaTotal) : "memory");
           } else {
             wait_all_vm();
           }
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          // The next slice's loads are spread between the rows of MFMAs, so no
-          // wave stalls on load issue before its first MFMA.
-          const bool more = kt + ST - 1 < KT;
-          int nxt = st + ST - 1;
-          if (nxt >= ST) nxt -= ST;
-          constexpr int kHooks = Tr::kSteps * SM;
-          auto hook = [&](int h) MOE_INLINE {
-            if (!more) return;
-#pragma unroll
-            for (int j = 0; j < Cfg::kDmaPerSlice; ++j)
-              if (j * kHooks / Cfg::kDmaPerSlice == h) issue_one(j, kt + ST - 1, nxt);
+          read_a(st, A0);
+          read_w(st, 0, w0);
+          auto body = [&](int kt, ASet& cur, ASet& nxt, auto last_tag) MOE_INLINE {
+            constexpr bool LAST = decltype(last_tag)::value;
+            read_w(st, 1, w1);
             __builtin_amdgcn_sched_barrier(0);
+            const bool more = kt + 2 < KT;
+            const int st2 = (st == 0) ? ST - 1 : st - 1;   // stage of slice kt+2
+            mma_half(0, cur, w0, [&](int t) MOE_INLINE {
+              if (!LAST && more) {
+#pragma unroll
+                for (int j = 0; j < Cfg::kDmaTotal; ++j)
+                  if (j * SM / Cfg::kDmaTotal == t) issue_one(j, kt + 2, st2);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            const int st1 = next_stage(st);
+            if constexpr (!LAST) {
+              // slice kt+1 has landed once only slice kt+2's loads are outstanding
+              if (more)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::kDmaTotal) : "memory");
+              else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+              __builtin_amdgcn_s_barrier();
+              asm volatile("" ::: "memory");
+              read_a(st1, nxt);
+              read_w(st1, 0, w0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            mma_half(1, cur, w1, [](int) MOE_INLINE {});
+            __builtin_amdgcn_sched_barrier(0);
+            st = st1;
           };
-          compute(full_tag, st, kt, has_tail && kt == KT - 1, hook);
-          st = (st + 1 == ST) ? 0 : st + 1;
-        }
-        gk += KT;
-        return;
-      }
-      uint4 ra0[Cfg::kAIters], rb0[Cfg::kBIters];
-      if constexpr (PF == 1) {
-        load_to(ra0, rb0, 0);
-        store_from(ra0, rb0, 0, 0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-          if (kt + 1 < KT) load_to(ra0, rb0, kt + 1);
-          compute(full_tag, kt & 1, kt, false, [](int) {});
-          if (kt + 1 < KT) store_from(ra0, rb0, (kt + 1) & 1, kt + 1);
-          __syncthreads();
+          using F_ = std::integral_constant<bool, false>;
+          using T_ = std::integral_constant<bool, true>;
+          int kt = 0;
+          for (; kt + 2 < KT; kt += 2) {
+            body(kt, A0, A1, F_{});
+            body(kt + 1, A1, A0, F_{});
+          }
+          if (kt + 2 == KT) {
+            body(kt, A0, A1, F_{});
+            body(kt + 1, A1, A0, T_{});
+          } else {
+            body(kt, A0, A1, T_{});
+          }
+          gk += KT;
         }
       } else {
-        uint4 ra1[Cfg::kAIters], rb1[Cfg::kBIters];
-        load_to(ra0, rb0, 0);
-        if (KT > 1) load_to(ra1, rb1, 1);
-        store_from(ra0, rb0, 0, 0);
-        __syncthreads();
-        for (int kt = 0; kt < KT; kt += 2) {
-          // slice kt is in LDS buffer 0; slice kt+1 is in flight in set 1
-          if (kt + 2 < KT) load_to(ra0, rb0, kt + 2);
-          compute(full_tag, 0, kt, false, [](int) {});
-          if (kt + 1 < KT) store_from(ra1, rb1, 1, kt + 1);
+        uint4 ra0[Cfg::kAIters], rb0[Cfg::kBIters];
+        if constexpr (PF == 1) {
+          load_to(ra0, rb0, 0);
+          store_from(ra0, rb0, 0, 0);
           __syncthreads();
-          if (kt + 1 >= KT) break;
-          // slice kt+1 is in LDS buffer 1; slice kt+2 is in flight in set 0
-          if (kt + 3 < KT) load_to(ra1, rb1, kt + 3);
-          compute(full_tag, 1, kt + 1, false, [](int) {});
-          if (kt + 2 < KT) store_from(ra0, rb0, 0, kt + 2);
+          for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 1 < KT) load_to(ra0, rb0, kt + 1);
+            compute(full_tag, kt & 1, kt, false);
+            if (kt + 1 < KT) store_from(ra0, rb0, (kt + 1) & 1, kt + 1);
+            __syncthreads();
+          }
+        } else {
+          uint4 ra1[Cfg::kAIters], rb1[Cfg::kBIters];
+          load_to(ra0, rb0, 0);
+          if (KT > 1) load_to(ra1, rb1, 1);
+          store_from(ra0, rb0, 0, 0);
           __syncthreads();
+          for (int kt = 0; kt < KT; kt += 2) {
+            // slice kt is in LDS buffer 0; slice kt+1 is in flight in set 1
+            if (kt + 2 < KT) load_to(ra0, rb0, kt + 2);
+            compute(full_tag, 0, kt, false);
+            if (kt + 1 < KT) store_from(ra1, rb1, 1, kt + 1);
+            __syncthreads();
+            if (kt + 1 >= KT) break;
+            // slice kt+1 is in LDS buffer 1; slice kt+2 is in flight in set 0
+            if (kt + 3 < KT) load_to(ra1, rb1, kt + 3);
+            compute(full_tag, 1, kt + 1, false);
+            if (kt + 2 < KT) store_from(ra0, rb0, 0, kt + 2);
+            __syncthreads();
+          }
         }
       }
     };
@@ -716,8 +783,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             wd[s] = cvt_e4m3x2(clamp448(v[4 * s] / scale), clamp448(v[4 * s + 1] / scale)) |
                     (cvt_e4m3x2(clamp448(v[4 * s + 2] / scale), clamp448(v[4 * s + 3] / scale)) << 16);
           uint8_t* dst = args.C + m * N_out + cbase;
-          static_assert(SNO == 4, "fp8 epilogue writes 16 codes per lane");
-          *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          static_assert(SNO == 2 || SNO == 4, "fp8 epilogue writes 8 or 16 codes per lane");
+          if constexpr (SNO == 4)
+            *reinterpret_cast<uint4*>(dst) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          else
+            *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
           if (wn == 0 && g == 0) args.c_scales[(long long)(n0 / 128) * args.M_rows + m] = scale;
         }
       } else if constexpr (CT == CType::BF16) {
