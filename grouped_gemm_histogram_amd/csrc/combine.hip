@@ -10,6 +10,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -26,34 +27,44 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       int H, int k, void* __restrict__ out_) {
   // Elements per lane per step: 8 for bf16 input (one 16-B load), 4 for f32.
   constexpr int EL = kBf16In ? 8 : 4;
+  constexpr int kUnroll = 2;   // column steps whose row loads are in flight together
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (t >= T) return;
   const int V = offsets[E];
-  for (int c0 = lane * EL; c0 < H; c0 += kWave * EL) {
-    float acc[EL];
-#pragma unroll
-    for (int i = 0; i < EL; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int p = row_pos[(size_t)t * k + j];
-      if (p < 0 || p >= V || p >= T * k) continue;
-      const float w = weights[(size_t)t * k + j];
-      if constexpr (kBf16In) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(y_) + (size_t)p * H + c0);
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(w, bf16_bits_to_f32(u[i] & 0xffffu), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(w, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
-        }
-      } else {
-        float v[4];
-        load16(static_cast<const float*>(y_) + (size_t)p * H + c0, v);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
-      }
+  // the token's k <= 16 slots, once: position (-1 if not a valid row) and weight of
+  // slot j, made wave-uniform while every lane is still active
+  int my_p = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    const int p = row_pos[(size_t)t * k + lane];
+    if (p >= 0 && p < V && p < T * k) {
+      my_p = p;
+      my_w = weights[(size_t)t * k + lane];
     }
+  }
+  constexpr int kMaxK = MOE_MAX_TOPK;   // k is validated against it at the boundary
+  int slot_p[kMaxK];
+  float slot_w[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    slot_p[j] = __builtin_amdgcn_readlane(my_p, j);
+    slot_w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+  }
+  auto load_row = [&](int p, int c0, float (&v)[EL]) {
+    if constexpr (kBf16In) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y_) + (size_t)p * H + c0);
+      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(u[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_f32(u[i] >> 16);
+      }
+    } else {
+      load16(static_cast<const float*>(y_) + (size_t)p * H + c0, v);
+    }
+  };
+  auto store_out = [&](int c0, const float (&acc)[EL]) {
     if constexpr (kBf16Out) {
       uint16_t* o = static_cast<uint16_t*>(out_) + (size_t)t * H + c0;
       if constexpr (EL == 8) {
@@ -68,6 +79,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       for (int i = 0; i < EL; i += 4)
         *reinterpret_cast<float4*>(o + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
     }
+  };
+  constexpr int STEP = kWave * EL;
+  for (int cb = lane * EL; cb < H; cb += kUnroll * STEP) {
+    float acc[kUnroll][EL];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < EL; ++i) acc[u][i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {   // slot order: the sum is deterministic
+      const int p = slot_p[j];
+      if (j >= k || p < 0) continue;
+      const float w = slot_w[j];
+      float v[kUnroll][EL];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (cb + u * STEP < H) load_row(p, cb + u * STEP, v[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (cb + u * STEP < H)
+#pragma unroll
+          for (int i = 0; i < EL; ++i) acc[u][i] = fmaf(w, v[u][i], acc[u][i]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (cb + u * STEP < H) store_out(cb + u * STEP, acc[u]);
   }
 }
 

@@ -639,6 +639,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
               for (int sl = 0; sl < SH; ++sl) {
                 const f32x4 cur = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     w[sl], x.a[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                // keep the previous MFMA's scaling after this MFMA's issue
+                __builtin_amdgcn_sched_barrier(0);
                 if (sl > 0) {
 #pragma unroll
                   for (int r = 0; r < 4; ++r) acc[t][h * SH + sl - 1][r] = fmaf(prev[r], f, acc[t][h * SH + sl - 1][r]);

@@ -45,12 +45,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist
                                                     int E, int* __restrict__ offsets) {
   __shared__ int tot[2][kMaxBins + 1];
   const int nb = E + 1;
+  // per bin, exclusive scan over chunks; counts are loaded kBatch at a time so
+  // the loads of a batch are in flight together
+  constexpr int kBatch = 16;
   for (int b = threadIdx.x; b < nb; b += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_hist[(size_t)c * nb + b];
-      chunk_hist[(size_t)c * nb + b] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * nb + b] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * nb + b] = run;
+        run += v[i];
+      }
     }
     tot[0][b] = run;
   }
@@ -66,7 +74,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist
   for (int b = threadIdx.x; b < nb; b += blockDim.x) {
     const int base = (b == 0) ? 0 : tot[src][b - 1];   // exclusive
     offsets[b] = base;                                  // offsets[E] = valid rows
-    for (int c = 0; c < nchunks; ++c) chunk_hist[(size_t)c * nb + b] += base;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * nb + b] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * nb + b] = v[i] + base;
+    }
   }
 }
 
@@ -84,10 +99,21 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const int r0 = blockIdx.x * kChunk;
   const int r1 = min(R, r0 + kChunk);
-  for (int base = r0; base < r1; base += kWave) {
+  // all of the chunk's ids are loaded up front (one round trip instead of one per step)
+  constexpr int kSteps = kChunk / kWave;
+  int keys[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int r = r0 + i * kWave + lane;
+    keys[i] = (r < r1) ? bin_of(ids[r], E) : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int base = r0 + i * kWave;
+    if (base >= r1) break;
     const int r = base + lane;
     const bool active = r < r1;
-    const int key = active ? bin_of(ids[r], E) : 0;
+    const int key = keys[i];
     uint64_t same = __ballot(active);
     for (int b = 0; b < id_bits; ++b) {
       const bool bit = (key >> b) & 1;

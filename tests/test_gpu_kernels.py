@@ -340,11 +340,12 @@ def test_grouped_gemm_fp8_exact():
 
 # ------------------------------------------------------------------------------------ combine
 
-@pytest.mark.parametrize("ydt,odt,H", [(torch.bfloat16, torch.bfloat16, 2880), (torch.float32, torch.float32, 132),
-                                       (torch.bfloat16, torch.float32, 64), (torch.float32, torch.bfloat16, 4)])
-def test_combine(ydt, odt, H):
-    say(f"combine {ydt}->{odt} H={H}")
-    T, E, k = 333, 12, 4
+@pytest.mark.parametrize("ydt,odt,H,k", [(torch.bfloat16, torch.bfloat16, 2880, 4), (torch.float32, torch.float32, 132, 4),
+                                         (torch.bfloat16, torch.float32, 64, 4), (torch.float32, torch.bfloat16, 4, 4),
+                                         (torch.bfloat16, torch.bfloat16, 1096, 16)])
+def test_combine(ydt, odt, H, k):
+    say(f"combine {ydt}->{odt} H={H} k={k}")
+    T, E = 333, (12 if k <= 12 else 20)
     ids, w, off, sr, rp = _routing(T, E, k, 1000, 9)
     R = T * k
     V = int(off[-1])
