@@ -1,5 +1,6 @@
 """MI355X-native MoE expert layer: routing, sentinel-aware offsets, permute,
-grouped GEMMs with fused SiLU*up, and combine, as hand-written HIP for gfx950
+grouped GEMMs with fused SiLU*up, and combine (and the layer's backward), as
+hand-written HIP for gfx950
 behind the C ABI in ``include/moe.h``.
 
 ``ops`` holds torch-tensor wrappers (argument marshalling only); ``_lib``
@@ -8,6 +9,9 @@ loads ``libmoe.so``; ``build`` compiles it.
 
 from ._lib import MoeKernels, load  # noqa: F401
 from .ops import (  # noqa: F401
+    Gradients,
+    backward,
+    backward_workspace_bytes,
     build_offsets,
     forward,
     forward_workspace_bytes,

@@ -48,6 +48,9 @@ SIGNATURES: dict[str, tuple] = {
     "moe_forward_workspace": (SZ, [I64, I64, I64, I32, I32, I32]),
     "moe_forward": (I32, [P, I32, P, P, P, P, P, I32, I64, I64, I64, I32, I32, I64, I32, P, I32,
                           ctypes.POINTER(MoeAux), P, SZ, P]),
+    "moe_backward_workspace": (SZ, [I64, I64, I64, I32, I32]),
+    "moe_backward": (I32, [P, P, P, I32, I64, I64, I64, I32, I32, P, P, P, P, P, P, P, P, I32, P, P, SZ,
+                           P]),
     "moe_status_string": (ctypes.c_char_p, [I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (I32, []),
@@ -65,6 +68,8 @@ class MoeKernels:
     unpermute_combine: Callable
     forward_workspace: Callable
     forward: Callable
+    backward_workspace: Callable
+    backward: Callable
     status_string: Callable
     last_error: Callable
     abi_version: Callable

@@ -329,4 +329,148 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   return ok();
 }
 
+// ---------------------------------------------------------------------------------- backward
+
 }  // extern "C"
+
+namespace {
+
+struct BwdLayout {
+  size_t koff, xp, gu, h, y, dy, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
+  long long ldd;   // row stride of the expert-padded transposes (elements)
+};
+
+BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
+  BwdLayout L{};
+  const long long R = T * k;
+  L.ldd = ((R + 64LL * E) + 63) / 64 * 64;   // >= sum over experts of round_up(M_e, 64)
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.koff = take((size_t)(E + 1) * 4);
+  L.xp = take((size_t)R * H * 2);
+  L.gu = take((size_t)R * 2 * I * 4);
+  L.h = take((size_t)R * I * 2);
+  L.y = take((size_t)R * H * 4);
+  L.dy = take((size_t)R * H * 2);
+  L.dh = take((size_t)R * I * 4);
+  L.dgu = take((size_t)R * 2 * I * 2);
+  L.dxp = take((size_t)R * H * 4);
+  L.ones = take((size_t)R * 4);
+  L.w13t = take((size_t)E * 2 * I * H * 2);
+  L.w2t = take((size_t)E * H * I * 2);
+  L.ta = take((size_t)(H > 2 * I ? H : 2 * I) * L.ldd * 2);
+  L.tb = take((size_t)(H > I ? H : I) * L.ldd * 2);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k) {
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
+    return 0;
+  return bwd_layout(T, H, I, E, k).total;
+}
+
+moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dtype_t dtype,
+                          int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                          const float* topk_weights, const int32_t* offsets,
+                          const int32_t* sorted_rows, const int32_t* row_pos, const void* dout,
+                          void* dx, void* dw13, void* dw2, moe_dtype_t grad_dtype,
+                          float* dtopk_weights, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (moe_status_t s = check_experts(E, k)) return s;
+  MOE_REQUIRE(dtype == MOE_BF16, "moe_backward covers bf16 layers (dtype must be MOE_BF16)");
+  MOE_REQUIRE(grad_dtype == MOE_F32 || grad_dtype == MOE_BF16, "grad_dtype must be MOE_F32 or MOE_BF16");
+  MOE_REQUIRE(T >= 0 && H > 0 && I > 0 && H % 8 == 0 && I % 8 == 0, "bad sizes (H, I multiples of 8)");
+  const BwdLayout L = bwd_layout(T, H, I, E, k);
+  const long long R = T * k;
+  // the transposes and the K-grouped GEMM address rows of ldd elements with 32-bit offsets
+  MOE_REQUIRE(R <= kMaxRows / 2 && (2 * I > H ? 2 * I : H) * L.ldd * 2 < 0xffffffffLL &&
+                  (long long)E * 2 * I * H <= 0x7fffffffLL,
+              "sizes exceed the backward's 32-bit addressing");
+  MOE_REQUIRE(dx && dw13 && dw2 && w13 && w2, "null pointer argument");
+  if (T > 0)
+    MOE_REQUIRE(x && dout && topk_weights && offsets && sorted_rows && row_pos, "null pointer argument");
+  MOE_REQUIRE(aligned16(dx) && aligned16(dw13) && aligned16(dw2) && aligned16(w13) && aligned16(w2) &&
+                  (T == 0 || (aligned16(x) && aligned16(dout))),
+              "tensors must be 16-byte aligned");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, L.total);
+  MOE_REQUIRE(aligned16(workspace), "workspace must be 16-byte aligned");
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t st = as_stream(stream);
+  int* koff = reinterpret_cast<int*>(ws + L.koff);
+  float* gu = reinterpret_cast<float*>(ws + L.gu);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  float* dh = reinterpret_cast<float*>(ws + L.dh);
+  float* dxp = reinterpret_cast<float*>(ws + L.dxp);
+  float* ones = reinterpret_cast<float*>(ws + L.ones);
+  const int gdt = grad_dtype;
+  auto gemm = [&](const void* A, const void* B, long long M, long long N, long long K, void* C, int cdt,
+                  const int* kof, long long lda, long long ldb, int nE, const int* offs) {
+    moe::GemmLaunch p{};
+    p.A = A;
+    p.B = B;
+    p.ab_dtype = MOE_BF16;
+    p.offsets = offs;
+    p.E = nE;
+    p.M_rows = M;
+    p.N = N;
+    p.K = K;
+    p.silu = false;
+    p.C = C;
+    p.c_dtype = cdt;
+    p.koff = kof;
+    p.lda = lda;
+    p.ldb = ldb;
+    return moe::launch_grouped_gemm(p, st);
+  };
+  hipError_t e = hipSuccess;
+  auto step = [&](hipError_t r) {
+    if (e == hipSuccess) e = r;
+  };
+  if (T == 0) {
+    // no rows: every weight gradient is zero (a fill kernel, not a memset node)
+    step(moe::launch_fill_f32(static_cast<float*>(dw13), (long long)E * 2 * I * H * esize(grad_dtype) / 4, 0.0f, st));
+    step(moe::launch_fill_f32(static_cast<float*>(dw2), (long long)E * H * I * esize(grad_dtype) / 4, 0.0f, st));
+    return launched(e, "backward");
+  }
+  // forward intermediates, recomputed: x_perm, gu = [g | u] (f32), h, y (f32)
+  step(moe::launch_pad_offsets(offsets, E, (int)R, koff, st));
+  step(moe::launch_permute_copy(x, (int)T, H * 2, k, sorted_rows, offsets, E, (int)R, ws + L.xp, st));
+  step(gemm(ws + L.xp, w13, R, 2 * I, H, gu, MOE_F32, nullptr, 0, 0, E, offsets));
+  step(moe::launch_silu_mul_rows(gu, offsets, E, (int)R, (int)I, ws + L.h, st));
+  step(gemm(ws + L.h, w2, R, H, I, y, MOE_F32, nullptr, 0, 0, E, offsets));
+  // routing-weight gradients and the scattered output gradient
+  if (dtopk_weights)
+    step(moe::launch_route_grad(dout, y, row_pos, offsets, E, (int)T, k, (int)H, dtopk_weights, st));
+  step(moe::launch_expand_rows(dout, topk_weights, sorted_rows, offsets, E, (int)T, k, (int)H, ws + L.dy, st));
+  // data gradients: dh = dy W2 (on W2^T), SiLU*up backward, dx_perm = dgu W13 (on W13^T)
+  step(moe::launch_transpose_bf16(w2, E, (int)H, (int)I, ws + L.w2t, st));
+  step(gemm(ws + L.dy, ws + L.w2t, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets));
+  step(moe::launch_silu_bwd_rows(dh, gu, offsets, E, (int)R, (int)I, ws + L.dgu, st));
+  step(moe::launch_transpose_bf16(w13, E, (int)(2 * I), (int)H, ws + L.w13t, st));
+  step(gemm(ws + L.dgu, ws + L.w13t, R, H, 2 * I, dxp, MOE_F32, nullptr, 0, 0, E, offsets));
+  step(moe::launch_fill_f32(ones, R, 1.0f, st));
+  step(moe::launch_combine(dxp, false, row_pos, ones, offsets, E, (int)T, (int)H, k, dx,
+                           grad_dtype == MOE_BF16, st));
+  // weight gradients: K-grouped GEMMs over each expert's rows, on expert-padded transposes
+  const int ldd = (int)L.ldd;
+  step(moe::launch_transpose_segments_bf16(ws + L.dy, (int)R, (int)H, offsets, koff, E, ws + L.ta, ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.h, (int)R, (int)I, offsets, koff, E, ws + L.tb, ldd, st));
+  step(gemm(ws + L.ta, ws + L.tb, H, I, ldd, dw2, gdt, koff, ldd, ldd, E, nullptr));
+  step(moe::launch_transpose_segments_bf16(ws + L.dgu, (int)R, (int)(2 * I), offsets, koff, E, ws + L.ta, ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.xp, (int)R, (int)H, offsets, koff, E, ws + L.tb, ldd, st));
+  step(gemm(ws + L.ta, ws + L.tb, 2 * I, H, ldd, dw13, gdt, koff, ldd, ldd, E, nullptr));
+  return launched(e, "backward");
+}
+
+}  // extern "C\"

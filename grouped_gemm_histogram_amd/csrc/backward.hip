@@ -1,0 +1,259 @@
+// backward.hip -- the elementwise and data-movement steps of the layer's backward
+// (bf16 layers).  The GEMMs of the backward run on grouped_gemm_kernel: the two
+// data-gradient products on transposed weights, the two weight-gradient
+// products in its K-grouped mode.
+//
+// The layer is the one of the LlamaFactory PR #10481 write-up (section 1):
+// h = SiLU(gate) * up per permuted row, y = W2 h, out[t] = sum_j w[t,j] y.  Its
+// backward, with the routing held fixed, is the chain rule through those steps;
+// sentinel rows take no part in it, and no output that a sentinel row would
+// own is left unwritten (the transformers PR #45621 write-up, section 3, traces
+// a training NaN to exactly that).
+//
+//   expand:       dy[p]  = w[r] * dout[r / k]           (p < V; r = sorted_rows[p])
+//   silu_mul:     h[p]   = silu(g) * u                  from the fp32 pre-activation gu
+//   silu_bwd:     dgu[p] = [dh * u * silu'(g), dh * silu(g)]
+//   route_grad:   dw[r]  = dout[r / k] . y[row_pos[r]]  (0 for a sentinel slot)
+//   transposes:   weights [E, R, C] -> [E, C, R]; permuted activations [R, C] ->
+//                 [C, Vp] with each expert's rows starting at a 64-aligned column
+//                 (koff[e]) and its padding columns zero, so that every expert's
+//                 K range is whole 64-element slices for the weight-gradient GEMM.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMaxE = 1024;
+
+__device__ __forceinline__ int clamp_off(const int* offsets, int e, int R) {
+  return min(max(offsets[e], 0), R);
+}
+
+__device__ __forceinline__ float bf16_at(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+
+}  // namespace
+
+// koff[e] = sum over e' < e of round_up(M_e', 64), e = 0..E.  One workgroup.
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int* __restrict__ offsets, int E, int R,
+                                                           int* __restrict__ koff) {
+  __shared__ int s[2][kMaxE + 1];
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    int m = 0;
+    if (e > 0) m = max(clamp_off(offsets, e, R) - clamp_off(offsets, e - 1, R), 0);
+    s[0][e] = (m + 63) & ~63;
+  }
+  __syncthreads();
+  int src = 0;
+  for (int d = 1; d <= E; d <<= 1) {   // inclusive scan over E+1 entries
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) s[src ^ 1][e] = s[src][e] + (e >= d ? s[src][e - d] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) koff[e] = s[src][e];
+}
+
+// 64x64 tiles through LDS; block (64, 4).  Batched: dst[b][c][r] = src[b][r][c].
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
+                                                             uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][66];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const size_t b = blockIdx.z;
+  const uint16_t* s = src + b * (size_t)R * C;
+  uint16_t* d = dst + b * (size_t)R * C;
+  const int x = threadIdx.x, y = threadIdx.y;
+  for (int r = y; r < 64; r += 4)
+    if (r0 + r < R && c0 + x < C) tile[r][x] = s[(size_t)(r0 + r) * C + c0 + x];
+  __syncthreads();
+  for (int c = y; c < 64; c += 4)
+    if (c0 + c < C && r0 + x < R) d[(size_t)(c0 + c) * R + r0 + x] = tile[x][c];
+}
+
+// Permuted rows [R, C] -> [C, ldd] in expert-padded column order: column
+// koff[e] + i holds row offsets[e] + i for i < M_e, and zero up to koff[e+1].
+// blockIdx.x walks 64-column blocks of the destination; a block lies inside one
+// expert's range since every koff[e] is a multiple of 64.
+__global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint16_t* __restrict__ src, int R,
+                                                                      int C, const int* __restrict__ offsets,
+                                                                      const int* __restrict__ koff, int E,
+                                                                      uint16_t* __restrict__ dst, int ldd) {
+  __shared__ uint16_t tile[64][66];
+  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int Vp = min(koff[E], ldd);
+  if (j0 >= Vp) return;
+  int lo = 0, hi = E;   // largest e with koff[e] <= j0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (koff[mid] <= j0) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int p0 = clamp_off(offsets, e, R) + (j0 - koff[e]);
+  const int pend = clamp_off(offsets, e + 1, R);
+  const int x = threadIdx.x, y = threadIdx.y;
+  for (int r = y; r < 64; r += 4) {
+    const int p = p0 + r;
+    tile[r][x] = (p < pend && c0 + x < C) ? src[(size_t)p * C + c0 + x] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int c = y; c < 64; c += 4)
+    if (c0 + c < C) dst[(size_t)(c0 + c) * ldd + j0 + x] = tile[x][c];
+}
+
+// h[p] = silu(g) * u for p < V, from gu = [g | u] fp32 [R, 2I]; 4 columns per thread.
+__global__ __launch_bounds__(256) void silu_mul_rows_kernel(const float* __restrict__ gu, const int* __restrict__ offsets,
+                                                            int E, int R, int I, uint16_t* __restrict__ h) {
+  const int V = clamp_off(offsets, E, R);
+  const long long n4 = (long long)V * (I / 4);
+  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (long long)gridDim.x * blockDim.x) {
+    const long long p = q / (I / 4);
+    const int c = (int)(q - p * (I / 4)) * 4;
+    const float4 g = *reinterpret_cast<const float4*>(gu + p * 2 * I + c);
+    const float4 u = *reinterpret_cast<const float4*>(gu + p * 2 * I + I + c);
+    *reinterpret_cast<uint2*>(h + p * I + c) =
+        make_uint2(pack_bf16x2(silu_mul(g.x, u.x), silu_mul(g.y, u.y)), pack_bf16x2(silu_mul(g.z, u.z), silu_mul(g.w, u.w)));
+  }
+}
+
+__device__ __forceinline__ float dsilu(float g) {
+  const float s = 1.0f / (1.0f + __expf(-g));
+  return s * (1.0f + g * (1.0f - s));
+}
+
+// dgu[p] = [dh * u * silu'(g), dh * silu(g)] for p < V; bf16 out.
+__global__ __launch_bounds__(256) void silu_bwd_rows_kernel(const float* __restrict__ dh, const float* __restrict__ gu,
+                                                            const int* __restrict__ offsets, int E, int R, int I,
+                                                            uint16_t* __restrict__ dgu) {
+  const int V = clamp_off(offsets, E, R);
+  const long long n4 = (long long)V * (I / 4);
+  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (long long)gridDim.x * blockDim.x) {
+    const long long p = q / (I / 4);
+    const int c = (int)(q - p * (I / 4)) * 4;
+    const float4 d = *reinterpret_cast<const float4*>(dh + p * I + c);
+    const float4 g = *reinterpret_cast<const float4*>(gu + p * 2 * I + c);
+    const float4 u = *reinterpret_cast<const float4*>(gu + p * 2 * I + I + c);
+    const float dg[4] = {d.x * u.x * dsilu(g.x), d.y * u.y * dsilu(g.y), d.z * u.z * dsilu(g.z), d.w * u.w * dsilu(g.w)};
+    const float du[4] = {d.x * silu_mul(g.x, 1.0f), d.y * silu_mul(g.y, 1.0f), d.z * silu_mul(g.z, 1.0f),
+                         d.w * silu_mul(g.w, 1.0f)};
+    *reinterpret_cast<uint2*>(dgu + p * 2 * I + c) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+    *reinterpret_cast<uint2*>(dgu + p * 2 * I + I + c) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+  }
+}
+
+// dy[p] = w[r] * dout[r / k] (bf16) for p < V; one wave per row, 8 columns per lane step.
+__global__ __launch_bounds__(256) void expand_rows_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ w,
+                                                          const int* __restrict__ sorted_rows, const int* __restrict__ offsets,
+                                                          int E, int T, int k, int H, uint16_t* __restrict__ dy) {
+  const int R = T * k;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (p >= clamp_off(offsets, E, R)) return;
+  const int r = sorted_rows[p];
+  if (r < 0 || r >= R) return;   // inconsistent permutation: leave the row unwritten
+  const float wr = w[r];
+  const uint4* s = reinterpret_cast<const uint4*>(dout + (size_t)(r / k) * H);
+  uint4* d = reinterpret_cast<uint4*>(dy + (size_t)p * H);
+  for (int c = lane; c < H / 8; c += kWave) {
+    const uint4 v = s[c];
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(wr * bf16_bits_to_f32(in[i] & 0xffffu), wr * bf16_bits_to_f32(in[i] >> 16));
+    d[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// dw[r] = dout[r / k] . y[row_pos[r]] over valid slots, 0 otherwise; one wave per slot.
+__global__ __launch_bounds__(256) void route_grad_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ y,
+                                                         const int* __restrict__ row_pos, const int* __restrict__ offsets,
+                                                         int E, int T, int k, int H, float* __restrict__ dw) {
+  const int R = T * k;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (r >= R) return;
+  const int V = clamp_off(offsets, E, R);
+  const int p = row_pos[r];
+  float acc = 0.0f;
+  if (p >= 0 && p < V) {
+    const uint16_t* dt = dout + (size_t)(r / k) * H;
+    const float* yp = y + (size_t)p * H;
+    for (int c = lane; c < H; c += kWave) acc = fmaf(bf16_at(dt + c), yp[c], acc);
+    acc = wave_sum(acc);
+  }
+  if (lane == 0) dw[r] = acc;
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, long long n, float v) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+namespace {
+dim3 grid1d(long long n, int per_block) {
+  long long b = (n + per_block - 1) / per_block;
+  return dim3((unsigned)(b < 1 ? 1 : (b > 65535LL * 32 ? 65535LL * 32 : b)));
+}
+}  // namespace
+
+hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, R, koff);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream) {
+  if (batch > 0 && R > 0 && C > 0)
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R + 63) / 64, (C + 63) / 64, batch), dim3(64, 4), 0, stream,
+                       static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
+                                          void* dst, int ldd, hipStream_t stream) {
+  if (R > 0 && C > 0)
+    hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(64, 4), 0, stream,
+                       static_cast<const uint16_t*>(src), R, C, offsets, koff, E, static_cast<uint16_t*>(dst), ldd);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_rows(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream) {
+  if (R > 0)
+    hipLaunchKernelGGL(silu_mul_rows_kernel, grid1d((long long)R * (I / 4), 256 * 8), dim3(256), 0, stream, gu,
+                       offsets, E, R, I, static_cast<uint16_t*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
+                                hipStream_t stream) {
+  if (R > 0)
+    hipLaunchKernelGGL(silu_bwd_rows_kernel, grid1d((long long)R * (I / 4), 256 * 8), dim3(256), 0, stream, dh, gu,
+                       offsets, E, R, I, static_cast<uint16_t*>(dgu));
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_rows(const void* dout, const float* w, const int* sorted_rows, const int* offsets, int E,
+                              int T, int k, int H, void* dy, hipStream_t stream) {
+  const long long R = (long long)T * k;
+  if (R > 0)
+    hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(dout), w, sorted_rows, offsets, E, T, k, H,
+                       static_cast<uint16_t*>(dy));
+  return hipGetLastError();
+}
+
+hipError_t launch_route_grad(const void* dout, const float* y, const int* row_pos, const int* offsets, int E, int T,
+                             int k, int H, float* dw, hipStream_t stream) {
+  const long long R = (long long)T * k;
+  if (R > 0)
+    hipLaunchKernelGGL(route_grad_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(dout), y, row_pos, offsets, E, T, k, H, dw);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, long long n, float v, hipStream_t stream) {
+  if (n > 0) hipLaunchKernelGGL(fill_f32_kernel, grid1d(n, 256 * 4), dim3(256), 0, stream, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -73,6 +73,13 @@ struct GemmArgs {
   float* c_scales;
   int N_out;    // columns of C
   int n_tiles;  // ceil(N_out / BN_out)
+  // K-grouped mode (weight gradients), when koff is set: C[e] [M_rows, N_out] =
+  // sum over k in [koff[e], koff[e+1]) of A[m][k] * B[n][k], for e < E; A is
+  // [M_rows, lda] and B [N, ldb] (row strides in elements), every koff entry a
+  // multiple of 64 and the columns in [koff[e], koff[e+1]) of both valid
+  const int* koff;
+  int lda;      // A row stride (elements); the M-grouped mode uses K
+  int ldb;      // B row stride (elements); the M-grouped mode uses K
 };
 
 #define MOE_INLINE __attribute__((always_inline))
@@ -210,8 +217,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   // can leave A or C even for inconsistent input
   auto off_at = [&](int e) MOE_INLINE { return min(max(offsets[e], 0), args.M_rows); };
 
+  const bool kg = args.koff != nullptr;   // K-grouped mode (wave-uniform)
+
   // ---- per-expert m-tile prefix (wave 0, serial per lane + shuffle scan)
-  if (wave == 0) {
+  if (wave == 0 && !kg) {
     const int per = (E + 63) / 64;
     const int e0 = lane * per;
     int local = 0;
@@ -237,17 +246,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   }
   __syncthreads();
 
-  const int total_mt = s_mt_pre[E];
   const int n_tiles = args.n_tiles;
-  const int total_tiles = total_mt * n_tiles;
+  const int mt_all = (args.M_rows + BM - 1) / BM;   // K-grouped mode: m-tiles of every expert
+  const int total_tiles = kg ? E * mt_all * n_tiles : s_mt_pre[E] * n_tiles;
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (int)((blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int)blockIdx.x;
 
   const int K = args.K;
-  const int k_bytes = K * Tr::kEsize;
-  const int KT = (k_bytes + kSliceBytes - 1) / kSliceBytes;
   const int N_out = args.N_out;
-  const long long lda = k_bytes;
+  // operand row strides in bytes (the M-grouped mode: K)
+  const uint32_t lda_b = (uint32_t)args.lda * Tr::kEsize;
+  const uint32_t ldb_b = (uint32_t)args.ldb * Tr::kEsize;
 
   // loader geometry: thread owns chunk (tid & 7) of rows (tid >> 3) + i * THREADS/8
   const int ld_ch = tid & 7;
@@ -260,20 +269,44 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
   int gk = 0;   // slices this workgroup has consumed (selects the direct-load stage)
   for (int tile = slot; tile < total_tiles; tile += G) {
-    // ---- decode tile -> (expert, n-tile, m-tile)
-    const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
-    int lo = 0, hi = E;             // largest e with s_mt_pre[e] <= q
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_mt_pre[mid] <= q) lo = mid; else hi = mid;
+    // ---- decode tile -> (expert, n-tile, m-tile); K-grouped mode: every expert has
+    // all m-tiles of A, and its own K range
+    int e, nt, ml, seg_end, m0, out_row0, k_bytes;
+    const uint8_t* a_src = args.A;
+    const uint8_t* b_exp;
+    if (kg) {
+      const int per_e = mt_all * n_tiles;
+      e = tile / per_e;
+      const int local = tile - e * per_e;
+      nt = local / mt_all;
+      ml = local - nt * mt_all;
+      seg_end = args.M_rows;
+      m0 = ml * BM;
+      out_row0 = e * args.M_rows + m0;   // C[e] follows C[e-1]
+      const int k0 = min(max(args.koff[e], 0), args.lda);
+      const int k1 = min(max(args.koff[e + 1], k0), args.lda);
+      k_bytes = (k1 - k0) * Tr::kEsize;
+      a_src = args.A + (long long)k0 * Tr::kEsize;
+      b_exp = args.B + (long long)k0 * Tr::kEsize;
+    } else {
+      const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
+      int lo = 0, hi = E;             // largest e with s_mt_pre[e] <= q
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_mt_pre[mid] <= q) lo = mid; else hi = mid;
+      }
+      e = lo;
+      const int mt_e = s_mt_pre[e + 1] - s_mt_pre[e];
+      const int local = tile - s_mt_pre[e] * n_tiles;
+      nt = local / mt_e;
+      ml = local - nt * mt_e;
+      seg_end = off_at(e + 1);
+      m0 = off_at(e) + ml * BM;
+      out_row0 = m0;
+      k_bytes = K * Tr::kEsize;
+      b_exp = args.B + (long long)e * args.N * ldb_b;
     }
-    const int e = lo;
-    const int mt_e = s_mt_pre[e + 1] - s_mt_pre[e];
-    const int local = tile - s_mt_pre[e] * n_tiles;
-    const int nt = local / mt_e;
-    const int ml = local - nt * mt_e;
-    const int seg_end = off_at(e + 1);
-    const int m0 = off_at(e) + ml * BM;
+    const int KT = (k_bytes + kSliceBytes - 1) / kSliceBytes;
     const int rows_valid = min(BM, seg_end - m0);
     const int n0 = nt * Cfg::kBNOut;
 
@@ -282,10 +315,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int i = 0; i < Cfg::kAIters; ++i) {
       const int r = min(m0 + ld_row0 + i * LD_ROW_STEP, seg_end - 1);
-      a_off[i] = (uint32_t)r * (uint32_t)k_bytes;
+      a_off[i] = (uint32_t)r * lda_b;
     }
     uint32_t b_off[Cfg::kBIters];
-    const uint8_t* b_exp = args.B + (long long)e * args.N * lda;
 #pragma unroll
     for (int i = 0; i < Cfg::kBIters; ++i) {
       const int qrow = ld_row0 + i * LD_ROW_STEP;          // LDS row within the weight tile
@@ -298,7 +330,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const int within = qq % SLAB;
       const int col = n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15);
       const int colc = min(col, N_out - 1);
-      b_off[i] = (uint32_t)(half * N_out + colc) * (uint32_t)k_bytes;
+      b_off[i] = (uint32_t)(half * N_out + colc) * ldb_b;
     }
 
     // Global loads always use an in-bounds address (the last chunk of the row
@@ -307,7 +339,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const int kb = min(kt * kSliceBytes + ld_ch * 16, k_bytes - 16);
 #pragma unroll
       for (int i = 0; i < Cfg::kAIters; ++i)
-        ra[i] = *reinterpret_cast<const uint4*>(args.A + a_off[i] + kb);
+        ra[i] = *reinterpret_cast<const uint4*>(a_src + a_off[i] + kb);
 #pragma unroll
       for (int i = 0; i < Cfg::kBIters; ++i)
         rb[i] = *reinterpret_cast<const uint4*>(b_exp + b_off[i] + kb);
@@ -403,7 +435,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         // stage of a slice follows the workgroup's running slice count gk, so the
         // first slices of the next tile never land in a stage that other waves
         // may still be reading.
-        const uint8_t* a_u = uniform_ptr(args.A);
+        const uint8_t* a_u = uniform_ptr(a_src);
         const uint8_t* b_u = uniform_ptr(b_exp);
         const uint32_t wave_u = uniform_u32((uint32_t)wave);
         const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&smem[0][0];
@@ -414,7 +446,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
         for (int j = 0; j < Cfg::kDmaA; ++j) {
           const int r = (wave * Cfg::kDmaA + j) * 8 + (lane >> 3);
-          rowA[j] = (uint32_t)min(m0 + r, seg_end - 1) * (uint32_t)k_bytes;
+          rowA[j] = (uint32_t)min(m0 + r, seg_end - 1) * lda_b;
         }
 #pragma unroll
         for (int j = 0; j < Cfg::kDmaB; ++j) {
@@ -427,7 +459,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           constexpr int SLAB = Cfg::kWNOut;
           const int within = qq % SLAB;
           const int col = min(n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
-          rowB[j] = (uint32_t)(half * N_out + col) * (uint32_t)k_bytes;
+          rowB[j] = (uint32_t)(half * N_out + col) * ldb_b;
         }
         // fp8 block scales of slice kt: the activation-scale waves load the scales of
         // tile rows wave*64 + lane (block-major layout: row-contiguous per K block;
@@ -746,10 +778,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         }
       }
     };
-    if (rows_valid >= BM)
-      k_loop(std::integral_constant<bool, true>{});
-    else
-      k_loop(std::integral_constant<bool, false>{});
+    // (K-grouped mode: an expert with no rows has K = 0; its tiles store zeros)
+    if (KT > 0) {
+      if (rows_valid >= BM)
+        k_loop(std::integral_constant<bool, true>{});
+      else
+        k_loop(std::integral_constant<bool, false>{});
+    }
 
     // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of tile row 16*(t*WM+wm) + ii
     const int cbase = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
@@ -757,7 +792,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     for (int t = 0; t < SM; ++t) {
       const int rloc = 16 * (t * WM + wm) + ii;
       const bool row_ok = rloc < rows_valid;
-      const long long m = (long long)m0 + rloc;
+      const long long m = (long long)out_row0 + rloc;
       float v[4 * SNO];
 #pragma unroll
       for (int s = 0; s < SNO; ++s)
@@ -830,7 +865,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   }
 
   // ---- sentinel rows [offsets[E], M_rows) of C: exact zeros (fp8 scales: 1.0)
-  {
+  if (!kg) {
     constexpr int kCEsize = (CT == CType::F32) ? 4 : (CT == CType::BF16 ? 2 : 1);
     const long long V = off_at(E);
     const long long rows = (long long)args.M_rows - V;
@@ -930,6 +965,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.C = static_cast<uint8_t*>(p.C);
   a.c_scales = p.c_scales;
   a.N_out = p.silu ? (int)(p.N / 2) : (int)p.N;
+  a.koff = p.koff;
+  a.lda = p.koff ? (int)p.lda : (int)p.K;
+  a.ldb = p.koff ? (int)p.ldb : (int)p.K;
+  if (p.koff && (p.ab_dtype != 1 || p.silu || p.c_dtype == 2)) return hipErrorInvalidValue;
 
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
   if (p.ab_dtype == 1) {

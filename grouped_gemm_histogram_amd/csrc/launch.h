@@ -33,9 +33,29 @@ struct GemmLaunch {
   void* C;
   int c_dtype;   // moe_dtype_t
   float* c_scales;
+  // K-grouped mode (bf16 operands, no SiLU, f32/bf16 C): when koff is set,
+  // C[e] [M_rows, N] = sum over k in [koff[e], koff[e+1]) of A[m][k] * B[n][k]
+  // for e < E, with row strides lda / ldb (elements) and koff entries
+  // multiples of 64; offsets is unused.  K is then the largest K range.
+  const int* koff = nullptr;
+  long long lda = 0, ldb = 0;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice);
+
+// backward steps (backward.hip)
+hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);
+hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream);
+hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
+                                          void* dst, int ldd, hipStream_t stream);
+hipError_t launch_silu_mul_rows(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream);
+hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
+                                hipStream_t stream);
+hipError_t launch_expand_rows(const void* dout, const float* w, const int* sorted_rows, const int* offsets, int E,
+                              int T, int k, int H, void* dy, hipStream_t stream);
+hipError_t launch_route_grad(const void* dout, const float* y, const int* row_pos, const int* offsets, int E, int T,
+                             int k, int H, float* dw, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, long long n, float v, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const float* weights,
                           const int* offsets, int E, int T, int H, int k, void* out, bool out_bf16,

@@ -235,3 +235,52 @@ def forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.
                        ctypes.byref(aux_c) if aux_c is not None else None, _p(workspace),
                        workspace.numel(), _stream(x)))
     return (out, aux_t) if return_aux else out
+
+
+@dataclass
+class Gradients:
+    dx: torch.Tensor              # [T, H]
+    dw13: torch.Tensor            # [E, 2I, H]
+    dw2: torch.Tensor             # [E, H, I]
+    dtopk_weights: torch.Tensor   # f32 [T, k]
+
+
+def backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return load().backward_workspace(T, H, I, E, k)
+
+
+def backward(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, dout: torch.Tensor,
+             topk_weights: torch.Tensor, offsets: torch.Tensor, sorted_rows: torch.Tensor,
+             row_pos: torch.Tensor, grad_dtype: torch.dtype = torch.float32,
+             workspace: Optional[torch.Tensor] = None) -> Gradients:
+    """Gradients of the bf16 layer for the routing ``forward`` chose (its aux outputs):
+    x, dout [T, H]; w13 [E, 2I, H]; w2 [E, H, I] -> dx, dw13, dw2 (grad_dtype), dtopk_weights (f32)."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    k = topk_weights.shape[1] if topk_weights.dim() == 2 else 1
+    dev = x.device
+    _need(w13, "w13", torch.bfloat16, (E, 2 * I, H), dev)
+    _need(w2, "w2", torch.bfloat16, (E, H, I), dev)
+    _need(dout, "dout", torch.bfloat16, (T, H), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, k), dev)
+    _need(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _need(sorted_rows, "sorted_rows", torch.int32, device=dev)
+    _need(row_pos, "row_pos", torch.int32, device=dev)
+    if sorted_rows.numel() != T * k or row_pos.numel() != T * k:
+        raise ValueError("sorted_rows and row_pos need T*k entries")
+    g = Gradients(torch.empty(T, H, dtype=grad_dtype, device=dev),
+                  torch.empty(E, 2 * I, H, dtype=grad_dtype, device=dev),
+                  torch.empty(E, H, I, dtype=grad_dtype, device=dev),
+                  torch.empty(T, k, dtype=torch.float32, device=dev))
+    lib = load()
+    need = lib.backward_workspace(T, H, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    _check(lib.backward(_p(x), _p(w13), _p(w2), _DT[torch.bfloat16], T, H, I, E, k, _p(topk_weights),
+                        _p(offsets), _p(sorted_rows), _p(row_pos), _p(dout), _p(g.dx), _p(g.dw13),
+                        _p(g.dw2), _DT[grad_dtype], _p(g.dtopk_weights), _p(workspace),
+                        workspace.numel(), _stream(x)))
+    return g

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -246,6 +246,49 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
                          int64_t I, int32_t E, int32_t k, int64_t num_valid_rows,
                          int32_t renormalize, void* out, moe_dtype_t out_dtype, moe_aux_t* aux,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace moe_backward needs (recomputed forward
+ * intermediates, gradient intermediates, transposed weights and the
+ * expert-padded transposed activations).  0 for invalid arguments. */
+size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k);
+
+/*
+ * moe_backward -- gradients of the bf16 layer computed by moe_forward, for
+ * the routing that forward chose (held fixed).  The pages trace a training
+ * NaN to sentinel outputs a kernel left uninitialised ([T45621] section 3):
+ * here sentinel rows take no part and every gradient element is written.
+ * With p = row_pos[r] the permuted position of routed slot r = t*k + j
+ * (valid iff p < offsets[E]) and e its expert:
+ *
+ *   dy_p   = w[r] * dout[t]                       (the weight is applied in the combine)
+ *   dw[r]  = dout[t] . y_p,   y_p = W2[e] (silu(g) * u),   [g | u] = W13[e] x_t
+ *   dh_p   = W2[e]^T dy_p,    dgu_p = [dh * u * silu'(g), dh * silu(g)]
+ *   dx[t]  = sum over the token's valid slots (ascending j) of W13[e]^T dgu_p
+ *   dW2[e] = sum over the expert's rows of dy_p h_p^T
+ *   dW13[e] = sum over the expert's rows of dgu_p x_t^T
+ *
+ * The forward pre-activations are recomputed here (the same grouped GEMMs as
+ * moe_forward, kept in f32); nothing of the forward's workspace is needed.
+ *
+ *   x, w13, w2, dout  MOE_BF16 (dtype must be MOE_BF16): x, dout [T, H];
+ *                w13 [E, 2I, H], w2 [E, H, I].  H and I multiples of 8.
+ *   topk_weights f32 [T, k], offsets [E+1], sorted_rows [T*k], row_pos [T*k]:
+ *                the routing of the forward (moe_aux_t of moe_forward, or
+ *                moe_route_topk + moe_build_offsets).
+ *   dx [T, H], dw13 [E, 2I, H], dw2 [E, H, I] of grad_dtype (MOE_F32 or
+ *                MOE_BF16): written in full (tokens with no valid slot and
+ *                experts with no rows get exact zeros).
+ *   dtopk_weights f32 [T, k]: dw; 0 for sentinel slots.  Nullable.
+ *   workspace    >= moe_backward_workspace(T, H, I, E, k) bytes.
+ * Accumulation is fp32; the MFMA operands dy, h, dgu and x are bf16.
+ */
+moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dtype_t dtype,
+                          int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                          const float* topk_weights, const int32_t* offsets,
+                          const int32_t* sorted_rows, const int32_t* row_pos, const void* dout,
+                          void* dx, void* dw13, void* dw2, moe_dtype_t grad_dtype,
+                          float* dtopk_weights, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Short name of a status code. */
 const char* moe_status_string(moe_status_t status);

@@ -19,6 +19,9 @@ fixes another precision):
 4. per-expert loop -- gate/up projection, SiLU(gate)*up, down projection,
                  on each expert's contiguous segment; sentinel rows zero.
 5. combine    -- routing-weight-scaled sum back to token order.
+6. backward   -- (``backward.py``) the gradients of steps 4-5 with the
+                 routing held fixed: dx, dW13, dW2 and the routing-weight
+                 gradients, by the chain rule through the same per-expert loop.
 
 Sources: the transformers PR #45621 write-up ("MoE 및 FP8 커널 최적화"),
 section 2 (sentinel tokens are excluded from the histogram / sorted as the

@@ -1,0 +1,179 @@
+"""Backward parity (moe_backward through the C ABI) against the backward oracle.
+
+The routing is the oracle's (computed on the host from the same logits) and is
+handed to the GPU, so the oracle never takes an input from the HIP path.
+Small bf16 layers are compared whole, element by element; the full-size
+gpt-oss-20b-shaped layer is compared on sampled experts (dW of an expert
+depends only on that expert's rows) and sampled tokens (dx and the routing-
+weight gradients of a token depend only on that token's slots), each through a
+reduced oracle problem holding exactly those rows.
+
+Tolerance, derived from the arithmetic.  The GPU feeds bf16 operands (dy, h,
+dgu and x, each rounded once: relative error <= 2^-9 of the element) to fp32
+MFMA accumulation.  An element of a product then errs by about 2^-9 times the
+magnitudes summed into it, not times its own value: dh[p, j] = sum_h dy[p, h]
+W2[h, j] can nearly cancel, and an element built from it (dgu, and a dW13 row
+of an expert with one routed row, which is dgu[p, j] x[p]) then carries that
+absolute error on a tiny value.  So every gradient is compared against the
+scale of its natural unit: dx per token row (the forward's convention), dW13
+and dW2 per expert matrix, the routing-weight gradients over all slots; each
+within 2e-2, a few 2^-9 with margin.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import HostExperts, np32, row_rel_err, say
+from oracle import backward as obwd, routing as orouting
+from oracle.layer import ExpertWeights
+from workloads import generate, get_config, small_variant
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-2
+
+SMALL = {
+    "gptoss20b_bf16": dict(T=384, H=712, I=456),
+    "sweep_bf16_v2048": dict(T=256, H=512, I=192),
+    "mixtral8x7b_bf16": dict(T=384, H=384, I=1408),
+}
+
+
+def _cfg(name):
+    base = get_config(name)
+    kw = dict(SMALL[name])
+    return small_variant(base, kw.pop("T")).replace(**kw)
+
+
+def _dout(T, H, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(T, H, generator=g).to(torch.bfloat16)
+
+
+def _routing(inp):
+    cfg = inp.cfg
+    ids, w = orouting.route_topk(inp.logits.cpu().numpy(), cfg.k, cfg.num_valid_rows, cfg.renormalize)
+    off, sr, rp = orouting.build_offsets(ids.reshape(-1), cfg.E)
+    return ids, w, off, sr, rp
+
+
+def _gpu_backward(inp, w, off, sr, rp, dout, grad_dtype=torch.float32):
+    import grouped_gemm_histogram_amd as g
+    T = inp.cfg.T
+    gr = g.backward(inp.x, inp.w13, inp.w2, dout.to(DEV),
+                    torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).reshape(T, -1).to(DEV),
+                    torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(rp).to(DEV),
+                    grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return gr
+
+
+def _per_expert(got, ref):
+    """max over experts of max|got - ref| / max|ref| over the expert's whole gradient matrix."""
+    E = ref.shape[0]
+    return row_rel_err(got.reshape(E, -1), ref.reshape(E, -1))
+
+
+def _weights(inp):
+    return ExpertWeights(HostExperts(inp.w13), HostExperts(inp.w2))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_small_layers(name):
+    cfg = _cfg(name)
+    say(f"backward {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} nv={cfg.num_valid_rows}")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dout = _dout(cfg.T, cfg.H, 21)
+    gr = _gpu_backward(inp, w, off, sr, rp, dout)
+    ref = obwd.backward(inp.x.float().cpu().numpy(), ids, w, _weights(inp), dout.float().numpy())
+    errs = {"dx": row_rel_err(np32(gr.dx), ref["dx"]),
+            "dw13": _per_expert(np32(gr.dw13), ref["dw13"]),
+            "dw2": _per_expert(np32(gr.dw2), ref["dw2"]),
+            "dw": row_rel_err(np32(gr.dtopk_weights).reshape(1, -1), ref["dw"].reshape(1, -1))}
+    say(f"  errors {errs}")
+    for key, err in errs.items():
+        assert err <= TOL, (key, err)
+    # sentinel slots: zero routing-weight gradient; tokens with no valid slot: zero dx
+    sentinel = ids >= cfg.E
+    assert np.all(np32(gr.dtopk_weights)[sentinel] == 0)
+    dead = sentinel.all(axis=1)
+    assert np.all(np32(gr.dx)[dead] == 0)
+    # experts with no rows: exactly zero weight gradients
+    empty = np.flatnonzero(np.diff(off) == 0)
+    for e in empty:
+        assert np.all(np32(gr.dw13)[e] == 0) and np.all(np32(gr.dw2)[e] == 0)
+
+
+def test_backward_bf16_grads_and_determinism():
+    cfg = _cfg("gptoss20b_bf16")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dout = _dout(cfg.T, cfg.H, 22)
+    a = _gpu_backward(inp, w, off, sr, rp, dout, torch.bfloat16)
+    b = _gpu_backward(inp, w, off, sr, rp, dout, torch.bfloat16)
+    for f in ("dx", "dw13", "dw2", "dtopk_weights"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    ref = obwd.backward(inp.x.float().cpu().numpy(), ids, w, _weights(inp), dout.float().numpy())
+    assert row_rel_err(np32(a.dx), ref["dx"]) <= TOL
+    assert _per_expert(np32(a.dw2), ref["dw2"]) <= TOL
+    assert _per_expert(np32(a.dw13), ref["dw13"]) <= TOL
+
+
+def test_backward_sentinel_rows_are_poison_proof():
+    """NaN in the inputs of tokens whose slots are all sentinel reaches no gradient."""
+    cfg = _cfg("sweep_bf16_v2048")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dead = (ids >= cfg.E).all(axis=1)
+    assert dead.any()
+    dout = _dout(cfg.T, cfg.H, 23)
+    clean = _gpu_backward(inp, w, off, sr, rp, dout)
+    x_p = inp.x.clone()
+    x_p[torch.from_numpy(dead).to(DEV)] = float("nan")
+    d_p = dout.clone()
+    d_p[torch.from_numpy(dead)] = float("nan")
+    poisoned = _gpu_backward(inp.__class__(inp.cfg, x_p, inp.logits, inp.w13, inp.w2), w, off, sr, rp, d_p)
+    for f in ("dx", "dw13", "dw2", "dtopk_weights"):
+        assert torch.equal(getattr(clean, f), getattr(poisoned, f)), f
+
+
+def test_backward_no_valid_rows():
+    cfg = _cfg("sweep_bf16_v2048").replace(num_valid_rows=0)
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    assert off[-1] == 0
+    gr = _gpu_backward(inp, w, off, sr, rp, _dout(cfg.T, cfg.H, 24))
+    for f in ("dx", "dw13", "dw2", "dtopk_weights"):
+        assert torch.count_nonzero(getattr(gr, f)).item() == 0, f
+
+
+def test_backward_full_size_sampled():
+    cfg = get_config("gptoss20b_bf16")
+    say(f"backward full size {cfg.name}")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dout = _dout(cfg.T, cfg.H, 25)
+    gr = _gpu_backward(inp, w, off, sr, rp, dout)
+    x_host = inp.x.float().cpu().numpy()
+    d_host = dout.float().numpy()
+    W = _weights(inp)
+    E = cfg.E
+    # sampled experts: a reduced problem holding exactly the expert's rows
+    for e in (0, E // 2 + 1):
+        keep = ids == e
+        toks = np.flatnonzero(keep.any(axis=1))
+        ids_e = np.where(keep[toks], ids[toks], E).astype(ids.dtype)
+        ref = obwd.backward(x_host[toks], ids_e, w[toks], W, d_host[toks])
+        e13 = row_rel_err(np32(gr.dw13[e]).reshape(1, -1), ref["dw13"][e].reshape(1, -1))
+        e2 = row_rel_err(np32(gr.dw2[e]).reshape(1, -1), ref["dw2"][e].reshape(1, -1))
+        say(f"  expert {e}: {len(toks)} rows, dw13 {e13:.2e} dw2 {e2:.2e}")
+        assert e13 <= TOL and e2 <= TOL
+    # sampled tokens: a reduced problem of those tokens with all their slots
+    toks = np.random.default_rng(26).choice(cfg.T, 24, replace=False)
+    ref = obwd.backward(x_host[toks], ids[toks], w[toks], W, d_host[toks])
+    ex = row_rel_err(np32(gr.dx)[toks], ref["dx"])
+    ew = row_rel_err(np32(gr.dtopk_weights)[toks], ref["dw"])
+    say(f"  tokens: dx {ex:.2e} dw {ew:.2e}")
+    assert ex <= TOL and ew <= TOL
