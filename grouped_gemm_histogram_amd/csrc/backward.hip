@@ -14,7 +14,7 @@
 //   silu_mul:     h[p]   = silu(g) * u                  from the fp32 pre-activation gu
 //   silu_bwd:     dgu[p] = [dh * u * silu'(g), dh * silu(g)]
 //   route_grad:   dw[r]  = dout[r / k] . y[row_pos[r]]  (0 for a sentinel slot)
-//   transposes:   weights [E, R, C] -> [E, C, R]; permuted activations [R, C] ->
+//   transposes:   weights [E, R, C] -> [E, C, R] (R, C multiples of 8); permuted activations [R, C] ->
 //                 [C, Vp] with each expert's rows starting at a 64-aligned column
 //                 (koff[e]) and its padding columns zero, so that every expert's
 //                 K range is whole 64-element slices for the weight-gradient GEMM.
@@ -55,31 +55,66 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int* __restrict
   for (int e = threadIdx.x; e <= E; e += blockDim.x) koff[e] = s[src][e];
 }
 
-// 64x64 tiles through LDS; block (64, 4).  Batched: dst[b][c][r] = src[b][r][c].
+// Transposes move 64x64 element tiles through LDS with 16-byte global loads and
+// stores (256 threads, two 8-element chunks each way).  In LDS, row r keeps its
+// 16-byte chunk q at position q ^ ((r >> 3) & 7), so that the column reads of the
+// second phase (lane = (column c, 8-row block b), eight rows 8b..8b+7 of one
+// column) spread over the banks.
+namespace {
+
+__device__ __forceinline__ int tp_pos(int r, int q) { return r * 64 + ((q ^ ((r >> 3) & 7)) << 3); }
+
+// Second phase: output chunk (c, b) = tile[8b .. 8b+7][c] as one 16-byte store.
+__device__ __forceinline__ uint4 tp_column(const uint16_t* tile, int c, int b) {
+  uint32_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * b + 2 * i;
+    const uint32_t lo = tile[tp_pos(r, c >> 3) + (c & 7)];
+    const uint32_t hi = tile[tp_pos(r + 1, c >> 3) + (c & 7)];
+    v[i] = lo | (hi << 16);
+  }
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+}  // namespace
+
+// Batched: dst[b][c][r] = src[b][r][c]; R and C multiples of 8.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
                                                              uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const size_t b = blockIdx.z;
-  const uint16_t* s = src + b * (size_t)R * C;
-  uint16_t* d = dst + b * (size_t)R * C;
-  const int x = threadIdx.x, y = threadIdx.y;
-  for (int r = y; r < 64; r += 4)
-    if (r0 + r < R && c0 + x < C) tile[r][x] = s[(size_t)(r0 + r) * C + c0 + x];
+  const size_t bz = blockIdx.z;
+  const uint16_t* s = src + bz * (size_t)R * C;
+  uint16_t* d = dst + bz * (size_t)R * C;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = t + 256 * h;            // chunk (row r, chunk q) of the source tile
+    const int r = idx >> 3, q = idx & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r0 + r < R && c0 + 8 * q < C) v = *reinterpret_cast<const uint4*>(s + (size_t)(r0 + r) * C + c0 + 8 * q);
+    *reinterpret_cast<uint4*>(tile + tp_pos(r, q)) = v;
+  }
   __syncthreads();
-  for (int c = y; c < 64; c += 4)
-    if (c0 + c < C && r0 + x < R) d[(size_t)(c0 + c) * R + r0 + x] = tile[x][c];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = t + 256 * h;            // output chunk (column c, row block b)
+    const int c = idx >> 3, b = idx & 7;
+    if (c0 + c < C && r0 + 8 * b < R)
+      *reinterpret_cast<uint4*>(d + (size_t)(c0 + c) * R + r0 + 8 * b) = tp_column(tile, c, b);
+  }
 }
 
 // Permuted rows [R, C] -> [C, ldd] in expert-padded column order: column
 // koff[e] + i holds row offsets[e] + i for i < M_e, and zero up to koff[e+1].
 // blockIdx.x walks 64-column blocks of the destination; a block lies inside one
-// expert's range since every koff[e] is a multiple of 64.
+// expert's range since every koff[e] is a multiple of 64.  C a multiple of 8.
 __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint16_t* __restrict__ src, int R,
                                                                       int C, const int* __restrict__ offsets,
                                                                       const int* __restrict__ koff, int E,
                                                                       uint16_t* __restrict__ dst, int ldd) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int Vp = min(koff[E], ldd);
   if (j0 >= Vp) return;
@@ -91,14 +126,23 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
   const int e = lo;
   const int p0 = clamp_off(offsets, e, R) + (j0 - koff[e]);
   const int pend = clamp_off(offsets, e + 1, R);
-  const int x = threadIdx.x, y = threadIdx.y;
-  for (int r = y; r < 64; r += 4) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = t + 256 * h;
+    const int r = idx >> 3, q = idx & 7;
     const int p = p0 + r;
-    tile[r][x] = (p < pend && c0 + x < C) ? src[(size_t)p * C + c0 + x] : (uint16_t)0;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (p < pend && c0 + 8 * q < C) v = *reinterpret_cast<const uint4*>(src + (size_t)p * C + c0 + 8 * q);
+    *reinterpret_cast<uint4*>(tile + tp_pos(r, q)) = v;
   }
   __syncthreads();
-  for (int c = y; c < 64; c += 4)
-    if (c0 + c < C) dst[(size_t)(c0 + c) * ldd + j0 + x] = tile[x][c];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = t + 256 * h;
+    const int c = idx >> 3, b = idx & 7;
+    if (c0 + c < C) *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * ldd + j0 + 8 * b) = tp_column(tile, c, b);
+  }
 }
 
 // h[p] = silu(g) * u for p < V, from gu = [g | u] fp32 [R, 2I]; 4 columns per thread.
@@ -204,7 +248,7 @@ hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipSt
 
 hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream) {
   if (batch > 0 && R > 0 && C > 0)
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R + 63) / 64, (C + 63) / 64, batch), dim3(64, 4), 0, stream,
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R + 63) / 64, (C + 63) / 64, batch), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
   return hipGetLastError();
 }
@@ -212,7 +256,7 @@ hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void*
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
                                           void* dst, int ldd, hipStream_t stream) {
   if (R > 0 && C > 0)
-    hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(64, 4), 0, stream,
+    hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), R, C, offsets, koff, E, static_cast<uint16_t*>(dst), ldd);
   return hipGetLastError();
 }
