@@ -49,6 +49,12 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             self.ev.append(h.value)
 
+    def record(self, i: int, stream: int) -> None:
+        """Record event i on a HIP stream handle (the stream the library's work is queued on)."""
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        if self.hip.hipEventRecord(self.ev[i], ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def ms(self, a: int, b: int) -> float:
         out = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
@@ -170,6 +176,37 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
             "sample": f"first {S} of {cfg.T} tokens, full weights (float64 per-expert loop)"}
 
 
+def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int) -> dict:
+    """moe_backward for the forward's routing, timed with HIP events on its stream.
+
+    GEMM work: 18*V*H*I flops, of which 6*V*H*I recompute the forward's pre-activations
+    and 12*V*H*I are the data- and weight-gradient products."""
+    dout = torch.randn(cfg.T, cfg.H, generator=torch.Generator(device="cuda:0").manual_seed(7),
+                       device="cuda:0").to(torch.bfloat16)
+    ws = torch.empty(g.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def call():
+        return g.backward(inp.x, inp.w13, inp.w2, dout, aux.topk_weights, aux.offsets, aux.sorted_rows,
+                          aux.row_pos, grad_dtype=torch.float32, workspace=ws)
+    for _ in range(max(1, warmup)):
+        call()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream   # the stream the wrappers queue on
+    ev.record(0, stream)
+    for _ in range(steps):
+        call()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(0, 1) / steps
+    ev.close()
+    V, H, I = cfg.V, cfg.H, cfg.I
+    return {"ms": ms, "grad_dtype": "f32", "workspace_bytes": ws.numel(),
+            "gemm_tflops_with_recompute": 18.0 * V * H * I / (ms * 1e-3) / 1e12,
+            "gemm_tflops_gradients_only": 12.0 * V * H * I / (ms * 1e-3) / 1e12}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +218,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--clamp-ab", action="store_true",
                     help="also time the staged layer with sentinel rows clamped onto the last expert")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing moe_backward (bf16 workloads time it by default)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -237,6 +276,10 @@ def main() -> int:
                              for i in range(args.steps)) / args.steps
     device_ms = sum(ev.ms(i * (nst + 1), i * (nst + 1) + nst) for i in range(args.steps)) / args.steps
     ev.close()
+
+    backward = None
+    if cfg.dtype == "bf16" and not args.no_backward:
+        backward = time_backward(g, torch, cfg, inp, aux, args.warmup, args.steps)
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -302,6 +345,8 @@ def main() -> int:
         "predicted_mfma_flops": {"gemm_gate_up": pred_gu, "gemm_down": pred_dn},
         "roofline": roofline,
     }
+    if backward is not None:
+        rec["backward"] = backward
     if args.clamp_ab:
         rec["clamp_ab"] = clamp_ab(g, cfg, inp, max(3, args.steps // 2))
     if not args.no_cpu_baseline:
