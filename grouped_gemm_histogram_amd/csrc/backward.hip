@@ -14,10 +14,11 @@
 //   silu_mul:     h[p]   = silu(g) * u                  from the fp32 pre-activation gu
 //   silu_bwd:     dgu[p] = [dh * u * silu'(g), dh * silu(g)]
 //   route_grad:   dw[r]  = dout[r / k] . y[row_pos[r]]  (0 for a sentinel slot)
-//   transposes:   weights [E, R, C] -> [E, C, R] (R, C multiples of 8); permuted activations [R, C] ->
-//                 [C, Vp] with each expert's rows starting at a 64-aligned column
-//                 (koff[e]) and its padding columns zero, so that every expert's
-//                 K range is whole 64-element slices for the weight-gradient GEMM.
+//   transposes:   weights [E, R, C] -> [E, C, R] (R, C multiples of 8); permuted
+//                 activations [R, C] -> expert-major blocks [C, round_up(M_e, 64)]
+//                 (rows of an expert contiguous, padding columns zero), so that every
+//                 expert's K range is whole 64-element slices for the weight-gradient
+//                 GEMM and each of its tiles reads a compact block.
 
 #include "device_common.h"
 #include "launch.h"
@@ -106,10 +107,12 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 }
 
-// Permuted rows [R, C] -> [C, ldd] in expert-padded column order: column
-// koff[e] + i holds row offsets[e] + i for i < M_e, and zero up to koff[e+1].
-// blockIdx.x walks 64-column blocks of the destination; a block lies inside one
-// expert's range since every koff[e] is a multiple of 64.  C a multiple of 8.
+// Permuted rows [R, C] -> expert-major transposed blocks: expert e's block is
+// [C, kpad_e] (kpad_e = koff[e+1] - koff[e] = round_up(M_e, 64)) at element
+// C * koff[e]; its column i holds row offsets[e] + i for i < M_e and zero
+// after.  blockIdx.x walks 64-column blocks of the padded column range
+// [0, koff[E]); a block lies inside one expert's range since every koff[e] is a
+// multiple of 64.  C a multiple of 8; koff[E] <= ldd bounds the grid.
 __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint16_t* __restrict__ src, int R,
                                                                       int C, const int* __restrict__ offsets,
                                                                       const int* __restrict__ koff, int E,
@@ -124,8 +127,11 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
     if (koff[mid] <= j0) lo = mid; else hi = mid;
   }
   const int e = lo;
-  const int p0 = clamp_off(offsets, e, R) + (j0 - koff[e]);
+  const int i0 = j0 - koff[e];                  // column of the expert's block
+  const int kpad = koff[e + 1] - koff[e];
+  const int p0 = clamp_off(offsets, e, R) + i0;
   const int pend = clamp_off(offsets, e + 1, R);
+  uint16_t* blk = dst + (size_t)C * koff[e];    // the expert's [C, kpad] block
   const int t = threadIdx.x;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
   for (int h = 0; h < 2; ++h) {
     const int idx = t + 256 * h;
     const int c = idx >> 3, b = idx & 7;
-    if (c0 + c < C) *reinterpret_cast<uint4*>(dst + (size_t)(c0 + c) * ldd + j0 + 8 * b) = tp_column(tile, c, b);
+    if (c0 + c < C) *reinterpret_cast<uint4*>(blk + (size_t)(c0 + c) * kpad + i0 + 8 * b) = tp_column(tile, c, b);
   }
 }
 

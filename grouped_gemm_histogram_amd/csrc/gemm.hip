@@ -74,9 +74,10 @@ struct GemmArgs {
   int N_out;    // columns of C
   int n_tiles;  // ceil(N_out / BN_out)
   // K-grouped mode (weight gradients), when koff is set: C[e] [M_rows, N_out] =
-  // sum over k in [koff[e], koff[e+1]) of A[m][k] * B[n][k], for e < E; A is
-  // [M_rows, lda] and B [N, ldb] (row strides in elements), every koff entry a
-  // multiple of 64 and the columns in [koff[e], koff[e+1]) of both valid
+  // A_e B_e^T for e < E, where A_e [M_rows, kpad_e] sits at element
+  // M_rows * koff[e] of A and B_e [N, kpad_e] at element N * koff[e] of B
+  // (expert-major blocks, rows of kpad_e = koff[e+1] - koff[e] elements, a
+  // multiple of 64)
   const int* koff;
   int lda;      // A row stride (elements); the M-grouped mode uses K
   int ldb;      // B row stride (elements); the M-grouped mode uses K
@@ -255,8 +256,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int K = args.K;
   const int N_out = args.N_out;
   // operand row strides in bytes (the M-grouped mode: K)
-  const uint32_t lda_b = (uint32_t)args.lda * Tr::kEsize;
-  const uint32_t ldb_b = (uint32_t)args.ldb * Tr::kEsize;
+  const uint32_t lda_all = (uint32_t)args.lda * Tr::kEsize;
+  const uint32_t ldb_all = (uint32_t)args.ldb * Tr::kEsize;
 
   // loader geometry: thread owns chunk (tid & 7) of rows (tid >> 3) + i * THREADS/8
   const int ld_ch = tid & 7;
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // ---- decode tile -> (expert, n-tile, m-tile); K-grouped mode: every expert has
     // all m-tiles of A, and its own K range
     int e, nt, ml, seg_end, m0, out_row0, k_bytes;
+    uint32_t kg_ld = 0;
     const uint8_t* a_src = args.A;
     const uint8_t* b_exp;
     if (kg) {
@@ -283,11 +285,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       seg_end = args.M_rows;
       m0 = ml * BM;
       out_row0 = e * args.M_rows + m0;   // C[e] follows C[e-1]
+      // koff is clamped to [0, lda] (lda bounds the padded column count)
       const int k0 = min(max(args.koff[e], 0), args.lda);
       const int k1 = min(max(args.koff[e + 1], k0), args.lda);
       k_bytes = (k1 - k0) * Tr::kEsize;
-      a_src = args.A + (long long)k0 * Tr::kEsize;
-      b_exp = args.B + (long long)k0 * Tr::kEsize;
+      a_src = args.A + (long long)args.M_rows * k0 * Tr::kEsize;
+      b_exp = args.B + (long long)args.N * k0 * Tr::kEsize;
+      kg_ld = (uint32_t)k_bytes;   // both blocks have rows of the expert's K
     } else {
       const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
       int lo = 0, hi = E;             // largest e with s_mt_pre[e] <= q
@@ -304,9 +308,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       m0 = off_at(e) + ml * BM;
       out_row0 = m0;
       k_bytes = K * Tr::kEsize;
-      b_exp = args.B + (long long)e * args.N * ldb_b;
+      b_exp = args.B + (long long)e * args.N * ldb_all;
     }
     const int KT = (k_bytes + kSliceBytes - 1) / kSliceBytes;
+    const uint32_t lda_b = kg ? kg_ld : lda_all;   // operand row strides of this tile (bytes)
+    const uint32_t ldb_b = kg ? kg_ld : ldb_all;
     const int rows_valid = min(BM, seg_end - m0);
     const int n0 = nt * Cfg::kBNOut;
 

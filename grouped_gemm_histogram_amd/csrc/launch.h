@@ -34,9 +34,10 @@ struct GemmLaunch {
   int c_dtype;   // moe_dtype_t
   float* c_scales;
   // K-grouped mode (bf16 operands, no SiLU, f32/bf16 C): when koff is set,
-  // C[e] [M_rows, N] = sum over k in [koff[e], koff[e+1]) of A[m][k] * B[n][k]
-  // for e < E, with row strides lda / ldb (elements) and koff entries
-  // multiples of 64; offsets is unused.  K is then the largest K range.
+  // C[e] [M_rows, N] = A_e B_e^T for e < E, with A_e [M_rows, kpad_e] at element
+  // M_rows * koff[e] of A and B_e [N, kpad_e] at element N * koff[e] of B
+  // (kpad_e = koff[e+1] - koff[e], a multiple of 64); offsets is unused and
+  // lda = ldb bound koff[E] (the padded column count).
   const int* koff = nullptr;
   long long lda = 0, ldb = 0;
 };
