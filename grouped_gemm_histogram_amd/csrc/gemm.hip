@@ -268,30 +268,34 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   // fragment read geometry
   const int rd_swz = swz(ii);
 
-  int gk = 0;   // slices this workgroup has consumed (selects the direct-load stage)
-  for (int tile = slot; tile < total_tiles; tile += G) {
-    // ---- decode tile -> (expert, n-tile, m-tile); K-grouped mode: every expert has
-    // all m-tiles of A, and its own K range
-    int e, nt, ml, seg_end, m0, out_row0, k_bytes;
-    uint32_t kg_ld = 0;
-    const uint8_t* a_src = args.A;
+  // ---- a tile's geometry: (expert, n-tile, m-tile) -> rows, K, operand bases.
+  // K-grouped mode: every expert has all m-tiles of A, and its own K range.
+  struct TileGeo {
+    int e, seg_end, m0, out_row0, k_bytes, KT, rows_valid, n0;
+    uint32_t lda_b, ldb_b;
+    const uint8_t* a_src;
     const uint8_t* b_exp;
+  };
+  auto decode = [&](int tile) MOE_INLINE {
+    TileGeo t;
+    int nt, ml;
+    t.a_src = args.A;
     if (kg) {
       const int per_e = mt_all * n_tiles;
-      e = tile / per_e;
-      const int local = tile - e * per_e;
+      t.e = tile / per_e;
+      const int local = tile - t.e * per_e;
       nt = local / mt_all;
       ml = local - nt * mt_all;
-      seg_end = args.M_rows;
-      m0 = ml * BM;
-      out_row0 = e * args.M_rows + m0;   // C[e] follows C[e-1]
+      t.seg_end = args.M_rows;
+      t.m0 = ml * BM;
+      t.out_row0 = t.e * args.M_rows + t.m0;   // C[e] follows C[e-1]
       // koff is clamped to [0, lda] (lda bounds the padded column count)
-      const int k0 = min(max(args.koff[e], 0), args.lda);
-      const int k1 = min(max(args.koff[e + 1], k0), args.lda);
-      k_bytes = (k1 - k0) * Tr::kEsize;
-      a_src = args.A + (long long)args.M_rows * k0 * Tr::kEsize;
-      b_exp = args.B + (long long)args.N * k0 * Tr::kEsize;
-      kg_ld = (uint32_t)k_bytes;   // both blocks have rows of the expert's K
+      const int k0 = min(max(args.koff[t.e], 0), args.lda);
+      const int k1 = min(max(args.koff[t.e + 1], k0), args.lda);
+      t.k_bytes = (k1 - k0) * Tr::kEsize;
+      t.a_src = args.A + (long long)args.M_rows * k0 * Tr::kEsize;
+      t.b_exp = args.B + (long long)args.N * k0 * Tr::kEsize;
+      t.lda_b = t.ldb_b = (uint32_t)t.k_bytes;   // both blocks have rows of the expert's K
     } else {
       const int q = tile / n_tiles;   // s_mt_pre[e] <= q identifies the expert
       int lo = 0, hi = E;             // largest e with s_mt_pre[e] <= q
@@ -299,22 +303,60 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         const int mid = (lo + hi) >> 1;
         if (s_mt_pre[mid] <= q) lo = mid; else hi = mid;
       }
-      e = lo;
-      const int mt_e = s_mt_pre[e + 1] - s_mt_pre[e];
-      const int local = tile - s_mt_pre[e] * n_tiles;
+      t.e = lo;
+      const int mt_e = s_mt_pre[t.e + 1] - s_mt_pre[t.e];
+      const int local = tile - s_mt_pre[t.e] * n_tiles;
       nt = local / mt_e;
       ml = local - nt * mt_e;
-      seg_end = off_at(e + 1);
-      m0 = off_at(e) + ml * BM;
-      out_row0 = m0;
-      k_bytes = K * Tr::kEsize;
-      b_exp = args.B + (long long)e * args.N * ldb_all;
+      t.seg_end = off_at(t.e + 1);
+      t.m0 = off_at(t.e) + ml * BM;
+      t.out_row0 = t.m0;
+      t.k_bytes = K * Tr::kEsize;
+      t.b_exp = args.B + (long long)t.e * args.N * ldb_all;
+      t.lda_b = lda_all;
+      t.ldb_b = ldb_all;
     }
-    const int KT = (k_bytes + kSliceBytes - 1) / kSliceBytes;
-    const uint32_t lda_b = kg ? kg_ld : lda_all;   // operand row strides of this tile (bytes)
-    const uint32_t ldb_b = kg ? kg_ld : ldb_all;
-    const int rows_valid = min(BM, seg_end - m0);
-    const int n0 = nt * Cfg::kBNOut;
+    t.KT = (t.k_bytes + kSliceBytes - 1) / kSliceBytes;
+    t.rows_valid = min(BM, t.seg_end - t.m0);
+    t.n0 = nt * Cfg::kBNOut;
+    return t;
+  };
+
+  // direct-load source rows of this wave for tile t: rowA[j] / rowB[j] are byte offsets
+  // of the row that lane i of load j fills (8-row groups; the weight rows follow the
+  // tile's LDS order, gate then up for SiLU, each wave slab's columns permuted)
+  auto dma_rows = [&](const TileGeo& t, uint32_t(&ra)[Cfg::kDmaA], uint32_t(&rb)[Cfg::kDmaB]) MOE_INLINE {
+#pragma unroll
+    for (int j = 0; j < Cfg::kDmaA; ++j) {
+      const int r = (wave * Cfg::kDmaA + j) * 8 + (lane >> 3);
+      ra[j] = (uint32_t)min(t.m0 + r, t.seg_end - 1) * t.lda_b;
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::kDmaB; ++j) {
+      const int qrow = (wave * Cfg::kDmaB + j) * 8 + (lane >> 3);
+      int half = 0, qq = qrow;
+      if constexpr (SILU) {
+        half = qrow / Cfg::kBNOut;
+        qq = qrow - half * Cfg::kBNOut;
+      }
+      constexpr int SLAB = Cfg::kWNOut;
+      const int within = qq % SLAB;
+      const int col = min(t.n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
+      rb[j] = (uint32_t)(half * N_out + col) * t.ldb_b;
+    }
+  };
+
+  int gk = 0;         // slices this workgroup has consumed (selects the direct-load stage)
+  bool pre = false;   // bf16: this tile's first slices were issued at the end of the previous one
+  for (int tile = slot; tile < total_tiles; tile += G) {
+    const TileGeo tg = decode(tile);
+    const int e = tg.e, seg_end = tg.seg_end, m0 = tg.m0, out_row0 = tg.out_row0, k_bytes = tg.k_bytes;
+    const int KT = tg.KT, rows_valid = tg.rows_valid, n0 = tg.n0;
+    const uint32_t lda_b = tg.lda_b, ldb_b = tg.ldb_b;
+    const uint8_t* a_src = tg.a_src;
+    const uint8_t* b_exp = tg.b_exp;
+    const bool pre_here = pre;
+    pre = false;
 
     // ---- byte offsets of this thread's source rows (A from its base, B from the expert's slab)
     uint32_t a_off[Cfg::kAIters];
@@ -449,24 +491,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         // i.e. logical chunk (i%8) ^ swz(row) = (i%8) ^ (i/8)
         const uint32_t cc = 16u * ((lane & 7) ^ (lane >> 3));
         uint32_t rowA[Cfg::kDmaA], rowB[Cfg::kDmaB];
-#pragma unroll
-        for (int j = 0; j < Cfg::kDmaA; ++j) {
-          const int r = (wave * Cfg::kDmaA + j) * 8 + (lane >> 3);
-          rowA[j] = (uint32_t)min(m0 + r, seg_end - 1) * lda_b;
-        }
-#pragma unroll
-        for (int j = 0; j < Cfg::kDmaB; ++j) {
-          const int qrow = (wave * Cfg::kDmaB + j) * 8 + (lane >> 3);
-          int half = 0, qq = qrow;
-          if constexpr (SILU) {
-            half = qrow / Cfg::kBNOut;
-            qq = qrow - half * Cfg::kBNOut;
-          }
-          constexpr int SLAB = Cfg::kWNOut;
-          const int within = qq % SLAB;
-          const int col = min(n0 + (qq - within) + slab_col<SNO>(within >> 4, within & 15), N_out - 1);
-          rowB[j] = (uint32_t)(half * N_out + col) * ldb_b;
-        }
+        dma_rows(tg, rowA, rowB);
         // fp8 block scales of slice kt: the activation-scale waves load the scales of
         // tile rows wave*64 + lane (block-major layout: row-contiguous per K block;
         // rows past the buffer repeat its last row), the others the weight scales
@@ -557,12 +582,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
                                                                   __builtin_bit_cast(bf16x8, a), acc[t][s], 0, 0, 0);
           };
           uint4 fa0[SM], fw0[SNB], fa1[SM], fw1[SNB];
-          issue(0, st);
-          if (KT > 1) {
-            issue(1, st == 2 ? 0 : st + 1);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
-          } else {
+          if (pre_here) {
+            // slices 0 and 1 were issued before the previous tile's epilogue, whose
+            // stores follow them on the counter: wait for everything
             wait_all_vm();
+          } else {
+            issue(0, st);
+            if (KT > 1) {
+              issue(1, st == 2 ? 0 : st + 1);
+              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
+            } else {
+              wait_all_vm();
+            }
           }
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
@@ -608,6 +639,31 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           };
           for (int kt = 0; kt + 1 < KT; ++kt) body(kt, std::integral_constant<bool, false>{});
           body(KT - 1, std::integral_constant<bool, true>{});
+          // Cross-tile prefetch: the next tile's first two slices are issued now, before
+          // this tile's epilogue, so their latency overlaps it.  They land in the stages
+          // of this workgroup's slices gk+KT-3 and gk+KT-2 (global count), which every
+          // wave finished reading before that slice's barrier, or, for a slice that is
+          // the last of its tile, before the next tile's first barrier.
+          const int tn = tile + G;
+          if (tn < total_tiles) {
+            const TileGeo nx = decode(tn);
+            if (nx.KT > 0) {
+              uint32_t nA[Cfg::kDmaA], nB[Cfg::kDmaB];
+              dma_rows(nx, nA, nB);
+              const uint8_t* na = uniform_ptr(nx.a_src);
+              const uint8_t* nb = uniform_ptr(nx.b_exp);
+              for (int s2 = 0; s2 < 2 && s2 < nx.KT; ++s2) {
+                const uint32_t o = min((uint32_t)(s2 * kSliceBytes) + cc, (uint32_t)(nx.k_bytes - 16));
+                const uint32_t sb = lds0 + (uint32_t)((gk + KT + s2) % ST) * Cfg::kStageBytes;
+#pragma unroll
+                for (int j = 0; j < Cfg::kDmaA; ++j) dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, na, nA[j] + o);
+#pragma unroll
+                for (int j = 0; j < Cfg::kDmaB; ++j)
+                  dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, nb, nB[j] + o);
+              }
+              pre = true;
+            }
+          }
           gk += KT;
         } else {
           static_assert(AB == AbType::FP8, "direct loads serve bf16 and fp8");
