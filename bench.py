@@ -1,6 +1,7 @@
 #!/usr/bin/env python3
-"""Benchmark of the MoE expert layer (route -> offsets -> permute -> gate/up GEMM
-+ SiLU*up -> down GEMM -> combine) on one MI355X.
+"""Benchmark of the MoE expert layer (route -> offsets -> gate/up GEMM + SiLU*up
+reading token rows through the permutation -> down GEMM -> combine; the fp8
+layer quantises token rows first) on one MI355X.
 
 One step = one moe_forward call over the whole synthetic batch, inputs already
 resident in HBM.  Prints one JSON line: layer tokens/s (value), per-stage
@@ -8,6 +9,10 @@ device times from HIP events recorded by the library between its stages, the
 grouped GEMMs' MFMA TFLOP/s against the dense peak, the roofline of the
 dominant kernel (the gate/up GEMM), and the CPU oracle timed on a bounded
 sample of the same workload.
+
+Warm-up (untimed) is at least --warmup steps and at least --warmup-seconds of
+work, so the timed steps run at the GPU's steady clock; the JSON "warmup" field
+is the number of warm-up steps made.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload gptoss20b_bf16]
 """
@@ -82,16 +87,22 @@ def load_traffic(workload: str):
     return entry.get("traffic_bytes")
 
 
+def tokens_with_rows(cfg) -> int:
+    """Tokens with at least one valid routed row (valid rows are a prefix of the flat rows)."""
+    return min(cfg.T, -(-cfg.V // cfg.k))
+
+
 def gate_up_bytes(cfg, offsets) -> float:
     """Algorithmic HBM bytes of one gate/up launch: each touched expert's W13 (and its
-    block scales) read once, the permuted activations read once, h written once."""
+    block scales) read once, each token row it gathers read once, h written once."""
     H, I, V = cfg.H, cfg.I, cfg.V
+    tv = tokens_with_rows(cfg)
     touched = sum(1 for e in range(cfg.E) if offsets[e + 1] > offsets[e])
     if cfg.dtype == "fp8":
         w = touched * (2 * I * H + (2 * I // 128) * (H // 128) * 4)
-        return w + V * H + V * (H // 128) * 4 + V * I + V * (I // 128) * 4
+        return w + tv * H + tv * (H // 128) * 4 + V * I + V * (I // 128) * 4
     esz = 4 if cfg.dtype == "f32" else 2
-    return touched * 2 * I * H * esz + V * H * esz + V * I * esz
+    return touched * 2 * I * H * esz + tv * H * esz + V * I * esz
 
 
 def predicted_mfma_flops(offsets, M_rows: int, n_out_total: int, K: int, tile) -> float:
@@ -122,8 +133,7 @@ def clamp_ab(g, cfg, inp, steps: int) -> dict:
         if clamp:
             ids = torch.where(ids >= E, torch.full_like(ids, E - 1), ids)
         off, sr, rp = g.build_offsets(ids, E)
-        xp = g.permute(inp.x, sr, off, k)
-        h = g.grouped_gemm(xp, inp.w13, off, "silu_mul")
+        h = g.grouped_gemm_gather(inp.x, inp.w13, off, sr, k, "silu_mul")
         y = g.grouped_gemm(h, inp.w2, off, "none")
         return g.unpermute_combine(y, rp, w, off, k)
     out = {}
@@ -176,7 +186,22 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
             "sample": f"first {S} of {cfg.T} tokens, full weights (float64 per-expert loop)"}
 
 
-def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int) -> dict:
+def warm(torch, call, at_least: int, seconds: float) -> int:
+    """Untimed warm-up: at least `at_least` calls and at least `seconds` of wall time, so that
+    the timed region starts at the GPU's steady clock (a cold MI355X runs the first few hundred
+    milliseconds of work measurably slower).  Returns the number of calls made."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < at_least or time.perf_counter() - t0 < seconds:
+        call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int, warm_s: float) -> dict:
     """moe_backward for the forward's routing, timed with HIP events on its stream.
 
     GEMM work: 18*V*H*I flops, of which 6*V*H*I recompute the forward's pre-activations
@@ -189,9 +214,7 @@ def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int) -> dict:
     def call():
         return g.backward(inp.x, inp.w13, inp.w2, dout, aux.topk_weights, aux.offsets, aux.sorted_rows,
                           aux.row_pos, grad_dtype=torch.float32, workspace=ws)
-    for _ in range(max(1, warmup)):
-        call()
-    torch.cuda.synchronize()
+    n_warm = warm(torch, call, max(1, warmup), warm_s)
     ev = HipEvents(2)
     stream = torch.cuda.current_stream().cuda_stream   # the stream the wrappers queue on
     ev.record(0, stream)
@@ -202,7 +225,7 @@ def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int) -> dict:
     ms = ev.ms(0, 1) / steps
     ev.close()
     V, H, I = cfg.V, cfg.H, cfg.I
-    return {"ms": ms, "grad_dtype": "f32", "workspace_bytes": ws.numel(),
+    return {"ms": ms, "steps": steps, "warmup": n_warm, "grad_dtype": "f32", "workspace_bytes": ws.numel(),
             "gemm_tflops_with_recompute": 18.0 * V * H * I / (ms * 1e-3) / 1e12,
             "gemm_tflops_gradients_only": 12.0 * V * H * I / (ms * 1e-3) / 1e12}
 
@@ -211,7 +234,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps before timing (at least)")
+    ap.add_argument("--warmup-seconds", type=float, default=2.0,
+                    help="warm-up also lasts at least this long (GPU clock ramp); 0 disables")
     ap.add_argument("--workload", default="gptoss20b_bf16")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens for the CPU oracle baseline (default: the whole layer)")
@@ -256,9 +281,7 @@ def main() -> int:
     torch.cuda.synchronize()
     offsets_host = aux.offsets.cpu().tolist()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    n_warm = warm(torch, step, args.warmup, args.warmup_seconds)
 
     nst = len(g._lib.FORWARD_STAGES)
     ev = HipEvents(args.steps * (nst + 1))
@@ -279,7 +302,7 @@ def main() -> int:
 
     backward = None
     if cfg.dtype == "bf16" and not args.no_backward:
-        backward = time_backward(g, torch, cfg, inp, aux, args.warmup, args.steps)
+        backward = time_backward(g, torch, cfg, inp, aux, args.warmup, args.steps, args.warmup_seconds)
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -294,8 +317,7 @@ def main() -> int:
     gu_tf = f_gu / (stage_ms["gemm_gate_up"] * 1e-3) / 1e12
     dn_tf = f_dn / (stage_ms["gemm_down"] * 1e-3) / 1e12
     gemm_tf = (f_gu + f_dn) / ((stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]) * 1e-3) / 1e12
-    tokens_valid = min(T, -(-V // k))
-    permute_bytes = (tokens_valid + V) * H * (esz if cfg.dtype != "fp8" else 2)
+    tokens_valid = tokens_with_rows(cfg)
     combine_bytes = V * H * esz + T * H * esz + 8 * T * k
     traffic = load_traffic(cfg.name)
     R = cfg.R
@@ -324,7 +346,7 @@ def main() -> int:
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": n_warm,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -339,12 +361,15 @@ def main() -> int:
         "gemm_down_tflops": dn_tf,
         "stage_ms": stage_ms,
         "device_ms_per_step": device_ms,
-        "permute_gbs": permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9,
         "combine_gbs": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
         "valid_rows_offsets_last": offsets_host[-1],
         "predicted_mfma_flops": {"gemm_gate_up": pred_gu, "gemm_down": pred_dn},
         "roofline": roofline,
     }
+    if cfg.dtype == "fp8":
+        # per-token quantisation: bf16 rows read, e4m3 codes and f32 scales written
+        q_bytes = T * H * 2 + T * H + T * (H // 128) * 4
+        rec["quantize_gbs"] = q_bytes / (stage_ms["act_staging"] * 1e-3) / 1e9
     if backward is not None:
         rec["backward"] = backward
     if args.clamp_ab:

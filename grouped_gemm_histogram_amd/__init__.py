@@ -16,8 +16,10 @@ from .ops import (  # noqa: F401
     forward,
     forward_workspace_bytes,
     grouped_gemm,
+    grouped_gemm_gather,
     grouped_gemm_tile_shape,
     permute,
+    quantize_rows,
     route_topk,
     unpermute_combine,
 )

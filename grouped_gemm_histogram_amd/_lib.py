@@ -32,7 +32,9 @@ class MoeAux(ctypes.Structure):
                 ("sorted_rows", P), ("row_pos", P), ("stage_events", ctypes.POINTER(P))]
 
 
-FORWARD_STAGES = ("route", "offsets", "permute", "gemm_gate_up", "gemm_down", "combine")
+# stage 3: nothing for f32/bf16 layers (the gate/up GEMM gathers token rows); per-token
+# quantisation for fp8
+FORWARD_STAGES = ("route", "offsets", "act_staging", "gemm_gate_up", "gemm_down", "combine")
 
 
 # name -> (restype, argtypes); mirrors include/moe.h
@@ -42,6 +44,9 @@ SIGNATURES: dict[str, tuple] = {
     "moe_build_offsets": (I32, [P, I64, I32, P, P, P, P, SZ, P]),
     "moe_permute": (I32, [P, I32, I64, I64, I32, P, P, I32, I64, P, I32, P, P]),
     "moe_grouped_gemm": (I32, [P, P, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P, P]),
+    "moe_grouped_gemm_gather": (I32, [P, P, I64, P, I32, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P,
+                                      P]),
+    "moe_quantize_rows": (I32, [P, I64, I64, P, P, P]),
     "moe_grouped_gemm_tile_shape": (I32, [I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32)]),
     "moe_unpermute_combine": (I32, [P, I32, P, P, P, I32, I64, I64, I32, P, I32, P]),
@@ -64,6 +69,8 @@ class MoeKernels:
     build_offsets: Callable
     permute: Callable
     grouped_gemm: Callable
+    grouped_gemm_gather: Callable
+    quantize_rows: Callable
     grouped_gemm_tile_shape: Callable
     unpermute_combine: Callable
     forward_workspace: Callable

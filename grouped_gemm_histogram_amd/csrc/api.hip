@@ -63,7 +63,7 @@ struct FwdLayout {
 FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dtype_t w_dtype) {
   const long long R = T * k;
   const bool fp8 = w_dtype == MOE_FP8_E4M3;
-  const size_t e_act = w_dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);  // x_perm and h
+  const size_t e_act = w_dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);  // h
   const size_t e_y = w_dtype == MOE_F32 ? 4 : 2;
   FwdLayout L{};
   size_t off = 0;
@@ -78,8 +78,8 @@ FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dt
   L.sorted = take(R * 4);
   L.rowpos = take(R * 4);
   L.offws = take(moe::build_offsets_workspace_bytes(R, E));
-  L.xp = take(R * H * e_act);
-  L.xps = take(fp8 ? R * (H / 128) * 4 : 0);
+  L.xp = take(fp8 ? T * H : 0);                     // fp8: quantised token rows
+  L.xps = take(fp8 ? T * (H / 128) * 4 : 0);
   L.h = take(R * I * e_act);
   L.hs = take(fp8 ? R * (I / 128) * 4 : 0);
   L.y = take(R * H * e_y);
@@ -164,10 +164,16 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t 
   return fail(MOE_ERR_UNSUPPORTED, "permute from dtype %d to dtype %d", (int)x_dtype, (int)perm_dtype);
 }
 
-moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* B,
-                              const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
-                              int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
-                              void* C, moe_dtype_t c_dtype, float* c_scales, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The grouped GEMM with A read directly (a_rows null) or gathered through a_rows.
+moe_status_t grouped_gemm_impl(const void* A, const float* a_scales, long long A_rows,
+                               const int32_t* a_rows, int32_t a_div, const void* B,
+                               const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
+                               int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
+                               void* C, moe_dtype_t c_dtype, float* c_scales, void* stream) {
   MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
   MOE_REQUIRE(valid_dtype(ab_dtype) && valid_dtype(c_dtype), "bad dtype");
   MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
@@ -189,10 +195,24 @@ moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* 
       return fail(MOE_ERR_UNSUPPORTED, "fp8 output is supported for fp8 operands with SiLU*up");
     MOE_REQUIRE(N_out % 128 == 0 && c_scales, "fp8 output needs N_out %% 128 == 0 and c_scales");
   }
+  if (a_rows) {
+    MOE_REQUIRE(a_div >= 1 && a_div <= MOE_MAX_TOPK, "gather_div=%d outside [1, %d]", a_div, MOE_MAX_TOPK);
+    MOE_REQUIRE(A_rows >= 0 && A_rows <= kMaxRows, "bad A_rows");
+    MOE_REQUIRE(A_rows * (K * esize(ab_dtype)) <= (long long)UINT32_MAX,
+                "gathered A must span under 4 GiB");
+  } else {
+    MOE_REQUIRE(M_rows * (K * esize(ab_dtype)) <= (long long)UINT32_MAX, "A must span under 4 GiB");
+  }
+  MOE_REQUIRE(N * (K * esize(ab_dtype)) <= (long long)UINT32_MAX, "one expert's B must span under 4 GiB");
   if (M_rows == 0) return ok();
   MOE_REQUIRE(A && B && offsets && C, "null pointer argument");
   MOE_REQUIRE(aligned16(A) && aligned16(B) && aligned16(C), "A, B and C must be 16-byte aligned");
+  if (a_rows && A_rows == 0)
+    return fail(MOE_ERR_INVALID_ARG, "gathered A has no rows but the product has %lld", (long long)M_rows);
   moe::GemmLaunch p{};
+  p.a_rows = a_rows;
+  p.a_div = a_div;
+  p.a_total = A_rows;
   p.A = A;
   p.a_scales = a_scales;
   p.B = B;
@@ -208,6 +228,41 @@ moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* 
   p.c_dtype = c_dtype;
   p.c_scales = c_scales;
   return launched(moe::launch_grouped_gemm(p, as_stream(stream)), "grouped_gemm");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* B,
+                              const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
+                              int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
+                              void* C, moe_dtype_t c_dtype, float* c_scales, void* stream) {
+  return grouped_gemm_impl(A, a_scales, M_rows, nullptr, 1, B, b_scales, ab_dtype, offsets, E, M_rows,
+                           N, K, epi, C, c_dtype, c_scales, stream);
+}
+
+moe_status_t moe_grouped_gemm_gather(const void* A, const float* a_scales, int64_t A_rows,
+                                     const int32_t* gather_rows, int32_t gather_div, const void* B,
+                                     const float* b_scales, moe_dtype_t ab_dtype,
+                                     const int32_t* offsets, int32_t E, int64_t M_rows, int64_t N,
+                                     int64_t K, moe_epilogue_t epi, void* C, moe_dtype_t c_dtype,
+                                     float* c_scales, void* stream) {
+  MOE_REQUIRE(gather_rows || M_rows == 0, "gather_rows is null");
+  return grouped_gemm_impl(A, a_scales, A_rows, gather_rows, gather_div, B, b_scales, ab_dtype, offsets, E,
+                           M_rows, N, K, epi, C, c_dtype, c_scales, stream);
+}
+
+moe_status_t moe_quantize_rows(const void* x, int64_t T, int64_t H, void* xq, float* xq_scales,
+                               void* stream) {
+  MOE_REQUIRE(T >= 0 && T <= kMaxRows && H > 0 && H <= kMaxRows, "bad sizes");
+  MOE_REQUIRE(H % 128 == 0, "fp8 quantisation needs H %% 128 == 0");
+  if (T == 0) return ok();
+  MOE_REQUIRE(x && xq && xq_scales, "null pointer argument");
+  MOE_REQUIRE(aligned16(x) && aligned16(xq), "x and xq must be 16-byte aligned");
+  return launched(moe::launch_permute_quant(x, (int)T, (int)H, 1, nullptr, nullptr, 0, (int)T, xq, xq_scales,
+                                            as_stream(stream)),
+                  "quantize_rows");
 }
 
 moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int32_t* tile_m,
@@ -311,11 +366,12 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   const moe_dtype_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   float* xps = fp8 ? reinterpret_cast<float*>(ws + L.xps) : nullptr;
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
-  if ((s = moe_permute(x, x_dtype, T, H, k, sorted, offs, E, R, ws + L.xp, act, xps, stream)))
-    return s;
+  // the gate/up GEMM reads token rows through the permutation; the fp8 layer
+  // quantises each token once first
+  if (fp8 && (s = moe_quantize_rows(x, T, H, ws + L.xp, xps, stream))) return s;
   if ((s = mark(3))) return s;
-  if ((s = moe_grouped_gemm(ws + L.xp, xps, w13, w13_scales, w_dtype, offs, E, R, 2 * I, H,
-                            MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream)))
+  if ((s = moe_grouped_gemm_gather(fp8 ? ws + L.xp : x, xps, T, sorted, k, w13, w13_scales, w_dtype, offs,
+                                   E, R, 2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream)))
     return s;
   if ((s = mark(4))) return s;
   if ((s = moe_grouped_gemm(ws + L.h, hs, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
@@ -336,7 +392,7 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
 namespace {
 
 struct BwdLayout {
-  size_t koff, xp, gu, h, y, dy, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
+  size_t koff, gu, h, y, dy, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
   long long ldd;   // row stride of the expert-padded transposes (elements)
 };
 
@@ -351,7 +407,6 @@ BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
     return at;
   };
   L.koff = take((size_t)(E + 1) * 4);
-  L.xp = take((size_t)R * H * 2);
   L.gu = take((size_t)R * 2 * I * 4);
   L.h = take((size_t)R * I * 2);
   L.y = take((size_t)R * H * 4);
@@ -415,8 +470,12 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
   float* ones = reinterpret_cast<float*>(ws + L.ones);
   const int gdt = grad_dtype;
   auto gemm = [&](const void* A, const void* B, long long M, long long N, long long K, void* C, int cdt,
-                  const int* kof, long long lda, long long ldb, int nE, const int* offs) {
+                  const int* kof, long long lda, long long ldb, int nE, const int* offs,
+                  const int* a_rows = nullptr) {
     moe::GemmLaunch p{};
+    p.a_rows = a_rows;
+    p.a_div = k;
+    p.a_total = T;
     p.A = A;
     p.B = B;
     p.ab_dtype = MOE_BF16;
@@ -443,10 +502,10 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
     step(moe::launch_fill_f32(static_cast<float*>(dw2), (long long)E * H * I * esize(grad_dtype) / 4, 0.0f, st));
     return launched(e, "backward");
   }
-  // forward intermediates, recomputed: x_perm, gu = [g | u] (f32), h, y (f32)
+  // forward intermediates, recomputed: gu = [g | u] (f32, token rows read through
+  // the permutation), h, y (f32)
   step(moe::launch_pad_offsets(offsets, E, (int)R, koff, st));
-  step(moe::launch_permute_copy(x, (int)T, H * 2, k, sorted_rows, offsets, E, (int)R, ws + L.xp, st));
-  step(gemm(ws + L.xp, w13, R, 2 * I, H, gu, MOE_F32, nullptr, 0, 0, E, offsets));
+  step(gemm(x, w13, R, 2 * I, H, gu, MOE_F32, nullptr, 0, 0, E, offsets, sorted_rows));
   step(moe::launch_silu_mul_rows(gu, offsets, E, (int)R, (int)I, ws + L.h, st));
   step(gemm(ws + L.h, w2, R, H, I, y, MOE_F32, nullptr, 0, 0, E, offsets));
   // routing-weight gradients and the scattered output gradient
@@ -464,11 +523,16 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
                            grad_dtype == MOE_BF16, st));
   // weight gradients: K-grouped GEMMs over each expert's rows, on expert-padded transposes
   const int ldd = (int)L.ldd;
-  step(moe::launch_transpose_segments_bf16(ws + L.dy, (int)R, (int)H, offsets, koff, E, ws + L.ta, ldd, st));
-  step(moe::launch_transpose_segments_bf16(ws + L.h, (int)R, (int)I, offsets, koff, E, ws + L.tb, ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.dy, (int)R, (int)H, offsets, koff, E, nullptr, 1, (int)R, ws + L.ta,
+                                           ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.h, (int)R, (int)I, offsets, koff, E, nullptr, 1, (int)R, ws + L.tb,
+                                           ldd, st));
   step(gemm(ws + L.ta, ws + L.tb, H, I, ldd, dw2, gdt, koff, ldd, ldd, E, nullptr));
-  step(moe::launch_transpose_segments_bf16(ws + L.dgu, (int)R, (int)(2 * I), offsets, koff, E, ws + L.ta, ldd, st));
-  step(moe::launch_transpose_segments_bf16(ws + L.xp, (int)R, (int)H, offsets, koff, E, ws + L.tb, ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.dgu, (int)R, (int)(2 * I), offsets, koff, E, nullptr, 1, (int)R,
+                                           ws + L.ta, ldd, st));
+  // x's rows of each expert, read through the permutation
+  step(moe::launch_transpose_segments_bf16(x, (int)R, (int)H, offsets, koff, E, sorted_rows, k, (int)T, ws + L.tb,
+                                           ldd, st));
   step(gemm(ws + L.ta, ws + L.tb, 2 * I, H, ldd, dw13, gdt, koff, ldd, ldd, E, nullptr));
   return launched(e, "backward");
 }

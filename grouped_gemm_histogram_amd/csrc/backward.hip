@@ -112,11 +112,15 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 // C * koff[e]; its column i holds row offsets[e] + i for i < M_e and zero
 // after.  blockIdx.x walks 64-column blocks of the padded column range
 // [0, koff[E]); a block lies inside one expert's range since every koff[e] is a
-// multiple of 64.  C a multiple of 8; koff[E] <= ldd bounds the grid.
+// multiple of 64.  C a multiple of 8; koff[E] <= ldd bounds the grid.  With
+// src_rows set, row p is read from row src_rows[p] / src_div of src (token rows
+// through the permutation; src has src_total rows, indices clamped into them).
 __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint16_t* __restrict__ src, int R,
                                                                       int C, const int* __restrict__ offsets,
                                                                       const int* __restrict__ koff, int E,
-                                                                      uint16_t* __restrict__ dst, int ldd) {
+                                                                      const int* __restrict__ src_rows, int src_div,
+                                                                      int src_total, uint16_t* __restrict__ dst,
+                                                                      int ldd) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int Vp = min(koff[E], ldd);
@@ -139,7 +143,10 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
     const int r = idx >> 3, q = idx & 7;
     const int p = p0 + r;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (p < pend && c0 + 8 * q < C) v = *reinterpret_cast<const uint4*>(src + (size_t)p * C + c0 + 8 * q);
+    if (p < pend && c0 + 8 * q < C) {
+      const int sr = src_rows != nullptr ? min(max(src_rows[p] / src_div, 0), src_total - 1) : p;
+      v = *reinterpret_cast<const uint4*>(src + (size_t)sr * C + c0 + 8 * q);
+    }
     *reinterpret_cast<uint4*>(tile + tp_pos(r, q)) = v;
   }
   __syncthreads();
@@ -260,10 +267,12 @@ hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void*
 }
 
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
-                                          void* dst, int ldd, hipStream_t stream) {
+                                          const int* src_rows, int src_div, int src_total, void* dst, int ldd,
+                                          hipStream_t stream) {
   if (R > 0 && C > 0)
     hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), R, C, offsets, koff, E, static_cast<uint16_t*>(dst), ldd);
+                       static_cast<const uint16_t*>(src), R, C, offsets, koff, E, src_rows, src_div > 0 ? src_div : 1,
+                       src_total, static_cast<uint16_t*>(dst), ldd);
   return hipGetLastError();
 }
 

@@ -81,6 +81,13 @@ struct GemmArgs {
   const int* koff;
   int lda;      // A row stride (elements); the M-grouped mode uses K
   int ldb;      // B row stride (elements); the M-grouped mode uses K
+  // Gathered A (M-grouped mode), when a_rows is set: row p of the product reads
+  // A row a_rows[p] / a_div of the a_total rows of A (token rows read through the
+  // permutation, so no permuted copy is made); a_scales is then [K/128, a_total].
+  // Without it, A has M_rows rows and row p is A row p (a_total = M_rows).
+  const int* a_rows;
+  int a_div;
+  int a_total;
 };
 
 #define MOE_INLINE __attribute__((always_inline))
@@ -206,17 +213,36 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   __shared__ float s_red[(CT == CType::FP8) ? WN * BM : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  int lane = tid & 63;
   const int wave = (int)__builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: lives in an SGPR
   const int wm = wave % WM;
   const int wn = wave / WM;
-  const int ii = lane & 15;   // MFMA row/column index of this lane
-  const int g = lane >> 4;    // MFMA k-group of this lane
+  int ii = lane & 15;         // MFMA row/column index of this lane
+  int g = lane >> 4;          // MFMA k-group of this lane
+  int rd_swz = swz(ii);       // fragment reads: swizzle of the lane's rows
+  // The lane index is made opaque to the compiler at the top of every tile and
+  // before every epilogue, so that values derived from it (load rows, epilogue
+  // columns) are recomputed there instead of being hoisted out of the tile loop
+  // and held in VGPRs through the K loop.  Held there, they pushed the fp8
+  // kernels into spills, and each spill reload waits for every outstanding
+  // load, the direct loads of the next slices included.
+  auto relane = [&]() MOE_INLINE {
+    asm volatile("" : "+v"(lane));
+    ii = lane & 15;
+    g = lane >> 4;
+    rd_swz = swz(ii);
+  };
   const int E = args.E;
   const int* __restrict__ offsets = args.offsets;
   // offsets as read from memory, clamped to [0, M_rows] so that no row index
   // can leave A or C even for inconsistent input
   auto off_at = [&](int e) MOE_INLINE { return min(max(offsets[e], 0), args.M_rows); };
+  // A row of product row p (p in [0, M_rows)); clamped so that an inconsistent
+  // permutation cannot leave A
+  auto a_row_of = [&](int p) MOE_INLINE {
+    if (args.a_rows == nullptr) return p;
+    return min(max(args.a_rows[p] / args.a_div, 0), args.a_total - 1);
+  };
 
   const bool kg = args.koff != nullptr;   // K-grouped mode (wave-uniform)
 
@@ -264,9 +290,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int ld_row0 = tid >> 3;
   constexpr int LD_ROW_STEP = THREADS / 8;
   const int ld_lds = ld_row0 * kSliceBytes + ((ld_ch ^ swz(ld_row0)) << 4);
-
-  // fragment read geometry
-  const int rd_swz = swz(ii);
 
   // ---- a tile's geometry: (expert, n-tile, m-tile) -> rows, K, operand bases.
   // K-grouped mode: every expert has all m-tiles of A, and its own K range.
@@ -329,7 +352,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int j = 0; j < Cfg::kDmaA; ++j) {
       const int r = (wave * Cfg::kDmaA + j) * 8 + (lane >> 3);
-      ra[j] = (uint32_t)min(t.m0 + r, t.seg_end - 1) * t.lda_b;
+      ra[j] = (uint32_t)a_row_of(min(t.m0 + r, t.seg_end - 1)) * t.lda_b;
     }
 #pragma unroll
     for (int j = 0; j < Cfg::kDmaB; ++j) {
@@ -349,6 +372,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   int gk = 0;         // slices this workgroup has consumed (selects the direct-load stage)
   bool pre = false;   // bf16: this tile's first slices were issued at the end of the previous one
   for (int tile = slot; tile < total_tiles; tile += G) {
+    relane();
     const TileGeo tg = decode(tile);
     const int e = tg.e, seg_end = tg.seg_end, m0 = tg.m0, out_row0 = tg.out_row0, k_bytes = tg.k_bytes;
     const int KT = tg.KT, rows_valid = tg.rows_valid, n0 = tg.n0;
@@ -363,7 +387,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
     for (int i = 0; i < Cfg::kAIters; ++i) {
       const int r = min(m0 + ld_row0 + i * LD_ROW_STEP, seg_end - 1);
-      a_off[i] = (uint32_t)r * lda_b;
+      a_off[i] = (uint32_t)a_row_of(r) * lda_b;
     }
     uint32_t b_off[Cfg::kBIters];
 #pragma unroll
@@ -494,16 +518,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         dma_rows(tg, rowA, rowB);
         // fp8 block scales of slice kt: the activation-scale waves load the scales of
         // tile rows wave*64 + lane (block-major layout: row-contiguous per K block;
-        // rows past the buffer repeat its last row), the others the weight scales
+        // rows past the buffer repeat its last row; gathered A: the scales of the
+        // row's A row), the others the weight scales
         // of (wave column q/2, half q%2) in lane q < 2*WN (other lanes repeat lane 0)
         const uint8_t* sc_u = nullptr;
         uint32_t sc_off = 0, sc_step = 0;
         if constexpr (Cfg::kLdsScales) {
           if (wave < Cfg::kScaleWaves) {
-            const int r = min(m0 + wave * 64 + lane, args.M_rows - 1);
+            const int r = a_row_of(min(m0 + wave * 64 + lane, args.M_rows - 1));
             sc_u = uniform_ptr(reinterpret_cast<const uint8_t*>(args.a_scales));
             sc_off = (uint32_t)r * 4u;
-            sc_step = (uint32_t)args.M_rows * 4u;
+            sc_step = (uint32_t)args.a_total * 4u;
           } else {
             const int q = lane < 2 * WN ? lane : 0;
             const int wq = q >> 1, hq = q & 1;
@@ -517,9 +542,28 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         }
         // load j of this wave for slice kt (j < kDmaA: activation rows; < kDmaPerSlice:
         // weight rows; fp8: then the block scales)
+        if constexpr (AB == AbType::FP8) {
+          // fp8 K is a multiple of 128 (whole slices): each lane's offset within a
+          // slice is fixed for the tile, and the slice offset goes into the scalar base
+#pragma unroll
+          for (int j = 0; j < Cfg::kDmaA; ++j) rowA[j] += cc;
+#pragma unroll
+          for (int j = 0; j < Cfg::kDmaB; ++j) rowB[j] += cc;
+        }
         auto issue_one = [&](int j, int kt, int stage) MOE_INLINE {
-          const uint32_t o = min((uint32_t)(kt * kSliceBytes) + cc, (uint32_t)(k_bytes - 16));
           const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kStageBytes;
+          if constexpr (AB == AbType::FP8) {
+            const uint32_t ko = (uint32_t)kt * kSliceBytes;
+            if (j < Cfg::kDmaA)
+              dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u + ko, rowA[j]);
+            else if (j < Cfg::kDmaPerSlice)
+              dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + (j - Cfg::kDmaA)) * 1024u, b_u + ko,
+                    rowB[j - Cfg::kDmaA]);
+            else
+              dma4(sb + Cfg::kTileBytes + wave_u * 256u, sc_u + (uint32_t)kt * sc_step, sc_off);
+            return;
+          }
+          const uint32_t o = min((uint32_t)(kt * kSliceBytes) + cc, (uint32_t)(k_bytes - 16));
           if (j < Cfg::kDmaA)
             dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + o);
           else if (j < Cfg::kDmaPerSlice)
@@ -581,6 +625,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[s]),
                                                                   __builtin_bit_cast(bf16x8, a), acc[t][s], 0, 0, 0);
           };
+          // the next tile's geometry and source rows are worked out now, so that the
+          // loads of a gathered A's row indices are long done when its first slices
+          // are issued at the end of this tile
+          const int tn = tile + G;
+          const bool has_next = tn < total_tiles;
+          TileGeo nx{};
+          uint32_t nA[Cfg::kDmaA], nB[Cfg::kDmaB];
+          if (has_next) {
+            nx = decode(tn);
+            dma_rows(nx, nA, nB);
+          }
           uint4 fa0[SM], fw0[SNB], fa1[SM], fw1[SNB];
           if (pre_here) {
             // slices 0 and 1 were issued before the previous tile's epilogue, whose
@@ -644,12 +699,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           // of this workgroup's slices gk+KT-3 and gk+KT-2 (global count), which every
           // wave finished reading before that slice's barrier, or, for a slice that is
           // the last of its tile, before the next tile's first barrier.
-          const int tn = tile + G;
-          if (tn < total_tiles) {
-            const TileGeo nx = decode(tn);
+          if (has_next) {
             if (nx.KT > 0) {
-              uint32_t nA[Cfg::kDmaA], nB[Cfg::kDmaB];
-              dma_rows(nx, nA, nB);
               const uint8_t* na = uniform_ptr(nx.a_src);
               const uint8_t* nb = uniform_ptr(nx.b_exp);
               for (int s2 = 0; s2 < 2 && s2 < nx.KT; ++s2) {
@@ -849,6 +900,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     }
 
     // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of tile row 16*(t*WM+wm) + ii
+    relane();
     const int cbase = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
 #pragma unroll
     for (int t = 0; t < SM; ++t) {
@@ -935,12 +987,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const long long row_bytes = (long long)N_out * kCEsize;
       const long long n16 = rows * row_bytes / 16;
       uint4* base = reinterpret_cast<uint4*>(args.C + V * row_bytes);
-      for (long long i = (long long)blockIdx.x * THREADS + tid; i < n16; i += (long long)G * THREADS)
+      int tz = tid;
+      asm volatile("" : "+v"(tz));   // computed here, not held through the tile loop
+      for (long long i = (long long)blockIdx.x * THREADS + tz; i < n16; i += (long long)G * THREADS)
         base[i] = make_uint4(0, 0, 0, 0);
       if constexpr (CT == CType::FP8) {
         // block-major scales [N_out/128, M_rows]: rows [V, M_rows) of every block
         const long long ns = rows * (N_out / 128);
-        for (long long i = (long long)blockIdx.x * THREADS + tid; i < ns; i += (long long)G * THREADS)
+        for (long long i = (long long)blockIdx.x * THREADS + tz; i < ns; i += (long long)G * THREADS)
           args.c_scales[(i / rows) * args.M_rows + V + (i % rows)] = 1.0f;
       }
     }
@@ -1031,6 +1085,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.lda = p.koff ? (int)p.lda : (int)p.K;
   a.ldb = p.koff ? (int)p.ldb : (int)p.K;
   if (p.koff && (p.ab_dtype != 1 || p.silu || p.c_dtype == 2)) return hipErrorInvalidValue;
+  a.a_rows = p.a_rows;
+  a.a_div = p.a_rows ? p.a_div : 1;
+  a.a_total = p.a_rows ? (int)p.a_total : (int)p.M_rows;
+  if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
   if (p.ab_dtype == 1) {

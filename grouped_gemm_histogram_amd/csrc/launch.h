@@ -16,6 +16,7 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
 
 hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
                                const int* offsets, int E, int R, void* xp, hipStream_t stream);
+// sorted_rows and offsets null: row p of xq is token row p, R = T rows
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
                                 hipStream_t stream);
@@ -40,6 +41,11 @@ struct GemmLaunch {
   // lda = ldb bound koff[E] (the padded column count).
   const int* koff = nullptr;
   long long lda = 0, ldb = 0;
+  // Gathered A (M-grouped mode only): row p of the product reads row
+  // a_rows[p] / a_div of A, which has a_total rows (a_scales [K/128, a_total]).
+  const int* a_rows = nullptr;
+  int a_div = 1;
+  long long a_total = 0;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice);
@@ -47,8 +53,10 @@ bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, 
 // backward steps (backward.hip)
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);
 hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream);
+// src_rows nullable: row p of the segments is src row src_rows[p] / src_div (of src_total)
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
-                                          void* dst, int ldd, hipStream_t stream);
+                                          const int* src_rows, int src_div, int src_total, void* dst, int ldd,
+                                          hipStream_t stream);
 hipError_t launch_silu_mul_rows(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream);
 hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
                                 hipStream_t stream);

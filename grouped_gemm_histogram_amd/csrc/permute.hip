@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 }
 
 // bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [H/128, R]; H % 128 == 0.
-// Each 16-lane group of the wave owns one 128-channel group per step.
+// Each 16-lane group of the wave owns one 128-channel group per step.  With
+// sorted_rows and offsets null, row p is token row p and all R = T rows are
+// written (the per-token quantisation alone, for a GEMM that gathers its rows).
 __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restrict__ x, int T,
                                                             int H, int k, const int* __restrict__ sorted_rows,
                                                             const int* __restrict__ offsets, int E,
@@ -45,8 +47,8 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restr
                                                             float* __restrict__ xs) {
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
-  if (p >= R || p >= offsets[E]) return;
-  const int src = sorted_rows[p] / k;
+  if (p >= R || (offsets != nullptr && p >= offsets[E])) return;
+  const int src = sorted_rows != nullptr ? sorted_rows[p] / k : p;
   if (src < 0 || src >= T) return;   // inconsistent permutation: leave the row unwritten
   const int n8 = H / 8;                       // 8-channel units per row
   const uint4* s = x + (size_t)src * n8;

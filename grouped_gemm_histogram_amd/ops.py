@@ -99,25 +99,23 @@ def permute(x: torch.Tensor, sorted_rows: torch.Tensor, offsets: torch.Tensor, k
     return (out, out_scales) if fp8 else out
 
 
-def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilogue: str = "none",
-                 a_scales: Optional[torch.Tensor] = None, b_scales: Optional[torch.Tensor] = None,
-                 out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-                 out_scales: Optional[torch.Tensor] = None):
-    """a [M, K] x b [E, N, K] over segments of offsets -> c [M, N or N/2] (+ scales for fp8 out).
-
-    fp8 activation scales (a_scales, and the returned scales) are block-major:
-    [K/128, M] and [N_out/128, M].
-    """
+def _gemm(a, b, offsets, epilogue, a_scales, b_scales, out_dtype, out, out_scales, gather):
     _need(a, "a", tuple(_DT))
-    M, K = a.shape
+    A_rows, K = a.shape
     E, N, K2 = b.shape
     if K2 != K:
         raise ValueError(f"K mismatch: a has {K}, b has {K2}")
     _need(b, "b", a.dtype, device=a.device)
     _need(offsets, "offsets", torch.int32, (E + 1,), a.device)
+    if gather is not None:
+        rows, div = gather
+        _need(rows, "gather_rows", torch.int32, device=a.device)
+        M = rows.numel()
+    else:
+        M = A_rows
     fp8 = a.dtype == torch.float8_e4m3fn
     if fp8:
-        _need(a_scales, "a_scales", torch.float32, (K // 128, M), a.device)
+        _need(a_scales, "a_scales", torch.float32, (K // 128, A_rows), a.device)
         _need(b_scales, "b_scales", torch.float32, (E, N // 128, K // 128), a.device)
     n_out = N // 2 if epilogue == "silu_mul" else N
     out_dtype = out_dtype or (torch.bfloat16 if fp8 else a.dtype)
@@ -127,11 +125,49 @@ def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilog
     fp8_out = out_dtype == torch.float8_e4m3fn
     if fp8_out and out_scales is None:
         out_scales = torch.empty(n_out // 128, M, dtype=torch.float32, device=a.device)
-    _check(load().grouped_gemm(_p(a), _p(a_scales) if fp8 else None, _p(b),
-                               _p(b_scales) if fp8 else None, _DT[a.dtype], _p(offsets), E, M, N, K,
-                               _EPI[epilogue], _p(out), _DT[out_dtype],
-                               _p(out_scales) if fp8_out else None, _stream(a)))
+    common = (_p(b), _p(b_scales) if fp8 else None, _DT[a.dtype], _p(offsets), E, M, N, K, _EPI[epilogue],
+              _p(out), _DT[out_dtype], _p(out_scales) if fp8_out else None, _stream(a))
+    if gather is None:
+        _check(load().grouped_gemm(_p(a), _p(a_scales) if fp8 else None, *common))
+    else:
+        _check(load().grouped_gemm_gather(_p(a), _p(a_scales) if fp8 else None, A_rows, _p(rows), int(div),
+                                          *common))
     return (out, out_scales) if fp8_out else out
+
+
+def grouped_gemm(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, epilogue: str = "none",
+                 a_scales: Optional[torch.Tensor] = None, b_scales: Optional[torch.Tensor] = None,
+                 out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                 out_scales: Optional[torch.Tensor] = None):
+    """a [M, K] x b [E, N, K] over segments of offsets -> c [M, N or N/2] (+ scales for fp8 out).
+
+    fp8 activation scales (a_scales, and the returned scales) are block-major:
+    [K/128, M] and [N_out/128, M].
+    """
+    return _gemm(a, b, offsets, epilogue, a_scales, b_scales, out_dtype, out, out_scales, None)
+
+
+def grouped_gemm_gather(a: torch.Tensor, b: torch.Tensor, offsets: torch.Tensor, gather_rows: torch.Tensor,
+                        gather_div: int, epilogue: str = "none", a_scales: Optional[torch.Tensor] = None,
+                        b_scales: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                        out: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None):
+    """grouped_gemm with product row p reading a[gather_rows[p] // gather_div]; c has gather_rows.numel() rows.
+
+    a [A_rows, K] holds token rows (a_scales [K/128, A_rows] for fp8); gather_rows is
+    sorted_rows of build_offsets and gather_div is k.
+    """
+    return _gemm(a, b, offsets, epilogue, a_scales, b_scales, out_dtype, out, out_scales,
+                 (gather_rows, gather_div))
+
+
+def quantize_rows(x: torch.Tensor):
+    """bf16 x [T, H] -> (e4m3 codes [T, H], f32 scales [H/128, T]), per row and 128 channels."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    xq = torch.empty(T, H, dtype=torch.float8_e4m3fn, device=x.device)
+    xs = torch.empty(H // 128, T, dtype=torch.float32, device=x.device)
+    _check(load().quantize_rows(_p(x), T, H, _p(xq), _p(xs), _stream(x)))
+    return xq, xs
 
 
 def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str = "none"):

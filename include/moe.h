@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -168,6 +168,45 @@ moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* 
                               void* stream);
 
 /*
+ * moe_grouped_gemm_gather -- moe_grouped_gemm whose A rows are read through a
+ * row map instead of from a permuted copy: the fusion of the scatter step into
+ * the GEMM's operand load (the pipeline of [LF10481] section 1 without its
+ * separate moe_scatter pass).
+ *
+ *   for p in [offsets[e], offsets[e+1]):
+ *       acc[p, n] = sum_k A[gather_rows[p] / gather_div, k] * B[e, n, k]
+ *
+ *   A            [A_rows, K] of ab_dtype: token rows (x of the layer, or its
+ *                per-token e4m3 codes from moe_quantize_rows).
+ *   a_scales     f32 [K/128, A_rows] for fp8 (the scales of A's rows).
+ *   gather_rows  device int32 [M_rows]: sorted_rows of moe_build_offsets.
+ *   gather_div   k: a flat routed row r belongs to token r / k.
+ *
+ * Everything else (B, offsets, epi, C, rows past offsets[E] written as zeros,
+ * errors) is as in moe_grouped_gemm; the results are bitwise identical to
+ * moe_permute followed by moe_grouped_gemm on the same inputs.  A row index
+ * outside [0, A_rows) (an inconsistent map) is clamped into it, so no read
+ * leaves A.  A must span under 4 GiB, and so must one expert's B.
+ */
+moe_status_t moe_grouped_gemm_gather(const void* A, const float* a_scales, int64_t A_rows,
+                                     const int32_t* gather_rows, int32_t gather_div, const void* B,
+                                     const float* b_scales, moe_dtype_t ab_dtype,
+                                     const int32_t* offsets, int32_t E, int64_t M_rows, int64_t N,
+                                     int64_t K, moe_epilogue_t epi, void* C, moe_dtype_t c_dtype,
+                                     float* c_scales, void* stream);
+
+/*
+ * moe_quantize_rows -- the per-token activation cast of [T45621] section 1
+ * (fp8_act_quant / per_token_cast_to_fp8) on token rows, once per token: bf16
+ * x [T, H] (H % 128 == 0) -> e4m3 codes xq [T, H] and scales xq_scales
+ * f32 [H/128, T], per row and 128 channels as in moe_permute.  The fp8 layer
+ * feeds it to moe_grouped_gemm_gather, so each token is quantised once rather
+ * than once per routed copy.
+ */
+moe_status_t moe_quantize_rows(const void* x, int64_t T, int64_t H, void* xq, float* xq_scales,
+                               void* stream);
+
+/*
  * moe_grouped_gemm_tile_shape -- the tile moe_grouped_gemm uses for a dtype and
  * epilogue: *tile_m activation rows by *tile_n weight rows (SiLU*up tiles
  * hold tile_n/2 gate and tile_n/2 up rows), *k_slice elements of K per step.
@@ -198,7 +237,7 @@ moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int
                                    moe_dtype_t out_dtype, void* stream);
 
 /* Stages of moe_forward, in launch order. */
-#define MOE_FORWARD_STAGES 6   /* route, offsets, permute, gate/up GEMM, down GEMM, combine */
+#define MOE_FORWARD_STAGES 6   /* route, offsets, activation staging, gate/up GEMM, down GEMM, combine */
 
 /* Optional caller-owned storage for the routing intermediates of moe_forward.
  * Each non-NULL pointer is used instead of workspace storage, so the caller
@@ -216,15 +255,18 @@ typedef struct {
   void** stage_events;    /* [MOE_FORWARD_STAGES + 1] hipEvent_t, or NULL */
 } moe_aux_t;
 
-/* Bytes of device workspace moe_forward needs (routing arrays, permuted
- * activations, h, per-row expert outputs). */
+/* Bytes of device workspace moe_forward needs (routing arrays, the fp8
+ * layer's quantised token rows, h, per-row expert outputs). */
 size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
                              moe_dtype_t w_dtype);
 
 /*
- * moe_forward -- the whole layer on one stream: route, offsets, permute,
- * grouped GEMM gate/up + SiLU*up, grouped GEMM down, combine ([LF10481]
- * section 1 pipeline; [T45621] section 2 sentinel exclusion).
+ * moe_forward -- the whole layer on one stream: route, offsets, grouped GEMM
+ * gate/up + SiLU*up reading token rows through the permutation
+ * (moe_grouped_gemm_gather), grouped GEMM down, combine ([LF10481] section 1
+ * pipeline with the scatter fused into the first GEMM's load; [T45621]
+ * section 2 sentinel exclusion).  The activation-staging stage is empty for
+ * f32 and bf16 layers and is moe_quantize_rows (once per token) for fp8.
  *
  *   x            [T, H]: MOE_F32 when w_dtype is MOE_F32, else MOE_BF16.
  *   router_logits f32 [T, E].
@@ -237,8 +279,9 @@ size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t
  *   workspace    >= moe_forward_workspace(...) bytes; no initialisation needed.
  *
  * Intermediates: f32 weights keep f32 throughout; bf16 weights round h and
- * the expert outputs to bf16; fp8 weights quantise the permuted activations
- * and h per row and 128 channels, and keep expert outputs in bf16.
+ * the expert outputs to bf16; fp8 weights quantise the token rows and h per
+ * row and 128 channels, and keep expert outputs in bf16.  Outputs are bitwise
+ * those of the unfused sequence moe_permute -> moe_grouped_gemm -> ...
  */
 moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router_logits,
                          const void* w13, const float* w13_scales, const void* w2,

@@ -82,7 +82,14 @@ def test_host_validation(lib):
     assert lib.permute(fake, 1, 4, 100, 2, fake, fake, 8, 8, fake, 2, None, None) == INVALID   # fp8 H%128
     assert lib.permute(fake, 2, 4, 128, 2, fake, fake, 8, 8, fake, 1, None, None) == INVALID   # x fp8
     assert lib.unpermute_combine(fake, 1, fake, fake, fake, 8, 4, 12, 2, fake, 1, None) == INVALID  # H*2 % 16
-    assert lib.forward_workspace(4096, 2880, 2880, 32, 4, 1) > 3 * 16384 * 2880 * 2
+    # gathered GEMM: a row map and a divisor in [1, 16] are required
+    assert lib.grouped_gemm_gather(fake, None, 64, None, 2, fake, None, 1, fake, 8, 128, 64, 64, 0, fake, 1,
+                                   None, None) == INVALID
+    assert lib.grouped_gemm_gather(fake, None, 64, fake, 0, fake, None, 1, fake, 8, 128, 64, 64, 0, fake, 1,
+                                   None, None) == INVALID
+    assert lib.quantize_rows(fake, 4, 100, fake, fake, None) == INVALID                       # H % 128
+    # h and the expert outputs (the gate/up GEMM reads token rows: no permuted copy)
+    assert lib.forward_workspace(4096, 2880, 2880, 32, 4, 1) > 2 * 16384 * 2880 * 2
     assert lib.forward(fake, 1, fake, fake, None, fake, None, 1, 16, 64, 64, 4, 2, -1, 1, fake, 1,
                        None, fake, 10, None) == WS
     assert lib.forward(fake, 0, fake, fake, None, fake, None, 1, 16, 64, 64, 4, 2, -1, 1, fake, 1,

@@ -338,6 +338,96 @@ def test_grouped_gemm_fp8_exact():
     assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
 
 
+# ------------------------------------------------------------------------------------ gathered GEMM
+
+GATHER_CASES = [
+    # dtype, T, E, k, valid rows (-1: all), N, K, epilogue
+    ("bf16", 300, 8, 4, -1, 2 * 456, 712, "silu_mul"),
+    ("bf16", 257, 16, 2, 300, 384, 256, "none"),
+    ("bf16", 64, 4, 2, 0, 128, 64, "silu_mul"),
+    ("bf16", 700, 3, 1, -1, 400, 200, "silu_mul"),
+    ("f32", 200, 6, 3, 450, 2 * 100, 96, "silu_mul"),
+    ("fp8", 200, 8, 4, 700, 512, 384, "silu_mul"),
+    ("fp8", 150, 5, 2, -1, 384, 256, "none"),
+]
+
+
+@pytest.mark.parametrize("dt,T,E,k,nv,N,K,epi", GATHER_CASES)
+def test_grouped_gemm_gather(dt, T, E, k, nv, N, K, epi):
+    """Token rows read through sorted_rows: oracle parity on the permuted rows, zeros past V,
+    and the same bits as permute + grouped_gemm."""
+    say(f"gather gemm {dt} T={T} E={E} k={k} nv={nv} N={N} K={K} {epi}")
+    ids, w, off, sr, rp = _routing(T, E, k, nv, T + N)
+    R, V = T * k, int(off[-1])
+    g = ops()
+    n_out = N // 2 if epi == "silu_mul" else N
+    d_off, d_sr = torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV)
+    kw = {}
+    if dt == "fp8":
+        aq, as_, bq, bs = _fp8_operands(T, E, N, K, T + N)
+        A, B = _u8_to_fp8(aq), _u8_to_fp8(bq)
+        kw = dict(a_scales=torch.from_numpy(np.ascontiguousarray(as_.T)).to(DEV),
+                  b_scales=torch.from_numpy(bs).to(DEV))
+        odt = torch.bfloat16
+        ref = ogemm.grouped_gemm(olayer.permute_rows(aq, sr, off, k), bq, off, epi,
+                                 olayer.permute_rows(as_, sr, off, k), bs)
+    else:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        gen = torch.Generator().manual_seed(T + K)
+        A = torch.randn(T, K, generator=gen).to(tdt)
+        B = (torch.randn(E, N, K, generator=gen) * 0.05).to(tdt)
+        ref = ogemm.grouped_gemm(olayer.permute_rows(A.float().numpy(), sr, off, k), B.float().numpy(), off, epi)
+        A, B, odt = A.to(DEV), B.to(DEV), tdt
+    C = torch.full((R, n_out), float("nan"), dtype=torch.float32, device=DEV).to(odt)
+    g.grouped_gemm_gather(A, B, d_off, d_sr, k, epi, out=C, **kw)
+    got = np32(C)
+    assert np.all(got[V:] == 0)
+    if V:
+        err = row_rel_err(got[:V], ref[:V])
+        say(f"  err {err:.3e}")
+        assert err <= TOL[dt]
+    # the unfused sequence gives the same bits
+    if dt == "fp8":
+        xp = torch.zeros(R, K, dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
+        xs = torch.ones(K // 128, R, dtype=torch.float32, device=DEV)
+        xp[:V] = A[d_sr[:V].long() // k]
+        xs[:, :V] = kw["a_scales"][:, d_sr[:V].long() // k]
+        C2 = g.grouped_gemm(xp, B, d_off, epi, a_scales=xs, b_scales=kw["b_scales"], out_dtype=odt)
+    else:
+        C2 = g.grouped_gemm(g.permute(A, d_sr, d_off, k, out=torch.zeros(R, K, dtype=A.dtype, device=DEV)),
+                            B, d_off, epi)
+    idt = torch.int16 if odt == torch.bfloat16 else torch.int32
+    assert torch.equal(C.cpu().view(idt), C2.cpu().view(idt))
+
+
+def test_grouped_gemm_gather_exact_bf16():
+    say("gather gemm exact bf16")
+    T, E, k, N, K = 400, 6, 3, 256, 384
+    ids, w, off, sr, rp = _routing(T, E, k, 1100, 31)
+    gen = torch.Generator().manual_seed(32)
+    A = torch.randint(-4, 5, (T, K), generator=gen).to(torch.bfloat16)
+    B = torch.randint(-4, 5, (E, N, K), generator=gen).to(torch.bfloat16)
+    g = ops()
+    C = g.grouped_gemm_gather(A.to(DEV), B.to(DEV), torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV),
+                              k, "none", out_dtype=torch.float32)
+    V = int(off[-1])
+    ref = ogemm.grouped_gemm(olayer.permute_rows(A.float().numpy(), sr, off, k), B.float().numpy(), off)
+    got = C.cpu().numpy()
+    assert np.array_equal(got[:V], ref.astype(np.float32)) and np.all(got[V:] == 0)
+
+
+@pytest.mark.parametrize("T,H", [(333, 1024), (1, 128), (64, 7168)])
+def test_quantize_rows(T, H):
+    say(f"quantize rows T={T} H={H}")
+    gen = torch.Generator().manual_seed(T + H)
+    x = (torch.randn(T, H, generator=gen) * torch.exp(torch.randn(T, 1, generator=gen))).to(torch.bfloat16)
+    x[T // 2, :128] = 0                                       # all-zero group: scale 1
+    q, s = ops().quantize_rows(x.to(DEV))
+    xq, xs = olayer.quant128(x.float().numpy())
+    assert np.array_equal(npu8(q), xq)
+    assert np.array_equal(np.ascontiguousarray(s.cpu().numpy().T).view(np.uint32), xs.view(np.uint32))
+
+
 # ------------------------------------------------------------------------------------ combine
 
 @pytest.mark.parametrize("ydt,odt,H,k", [(torch.bfloat16, torch.bfloat16, 2880, 4), (torch.float32, torch.float32, 132, 4),
