@@ -201,6 +201,41 @@ def warm(torch, call, at_least: int, seconds: float) -> int:
     return n
 
 
+def time_decode(g, torch, cfg, inp, steps: int, tokens=(1, 8, 64)) -> list:
+    """The layer at decode sizes on the same weights: the first T tokens of the batch.  These
+    launches take the 16-row decode tiles; the bound is streaming each touched expert's weights
+    once, so the rate reported is touched-weight bytes per layer time against 8 TB/s."""
+    res = []
+    esz = 4 if cfg.dtype == "f32" else 2
+    for T in tokens:
+        c = cfg.replace(T=T)
+        x, lg = inp.x[:T].contiguous(), inp.logits[:T].contiguous()
+        ws = torch.empty(g.forward_workspace_bytes(T, c.H, c.I, c.E, c.k, inp.w13.dtype), dtype=torch.uint8,
+                         device=x.device)
+        out = torch.empty(T, c.H, dtype=inp.x.dtype, device=x.device)
+        _, aux = g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, out=out, workspace=ws, return_aux=True)
+        off = aux.offsets.cpu().tolist()
+        touched = sum(1 for e in range(c.E) if off[e + 1] > off[e])
+
+        def call():
+            g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, out=out, workspace=ws)
+        warm(torch, call, 5, 0.3)
+        ev = HipEvents(2)
+        stream = torch.cuda.current_stream().cuda_stream
+        n = max(steps, 50)
+        ev.record(0, stream)
+        for _ in range(n):
+            call()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        us = ev.ms(0, 1) / n * 1e3
+        ev.close()
+        wbytes = touched * 3 * c.I * c.H * esz
+        res.append({"T": T, "experts_touched": touched, "us_per_layer": us,
+                    "weight_gbs": wbytes / (us * 1e-6) / 1e9, "frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+    return res
+
+
 def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int, warm_s: float) -> dict:
     """moe_backward for the forward's routing, timed with HIP events on its stream.
 
@@ -243,6 +278,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--clamp-ab", action="store_true",
                     help="also time the staged layer with sentinel rows clamped onto the last expert")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-size layer timings")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing moe_backward (bf16 workloads time it by default)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -300,6 +336,10 @@ def main() -> int:
     device_ms = sum(ev.ms(i * (nst + 1), i * (nst + 1) + nst) for i in range(args.steps)) / args.steps
     ev.close()
 
+    decode = None
+    if cfg.dtype == "bf16" and not args.no_decode:
+        decode = time_decode(g, torch, cfg, inp, args.steps)
+
     backward = None
     if cfg.dtype == "bf16" and not args.no_backward:
         backward = time_backward(g, torch, cfg, inp, aux, args.warmup, args.steps, args.warmup_seconds)
@@ -321,9 +361,9 @@ def main() -> int:
     combine_bytes = V * H * esz + T * H * esz + 8 * T * k
     traffic = load_traffic(cfg.name)
     R = cfg.R
-    pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none"))
+    pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none", R, E))
     # SiLU*up tiles hold tile_n/2 output columns: count them against N_out = I
-    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul")
+    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul", R, E)
     pred_gu = predicted_mfma_flops(offsets_host, R, I, H, (tm, tn // 2, ks)) * 2
 
     # The dominant kernel's bound: the larger of its MFMA time and its HBM time at peak.
@@ -370,6 +410,8 @@ def main() -> int:
         # per-token quantisation: bf16 rows read, e4m3 codes and f32 scales written
         q_bytes = T * H * 2 + T * H + T * (H // 128) * 4
         rec["quantize_gbs"] = q_bytes / (stage_ms["act_staging"] * 1e-3) / 1e9
+    if decode is not None:
+        rec["decode"] = decode
     if backward is not None:
         rec["backward"] = backward
     if args.clamp_ab:

@@ -265,12 +265,13 @@ moe_status_t moe_quantize_rows(const void* x, int64_t T, int64_t H, void* xq, fl
                   "quantize_rows");
 }
 
-moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int32_t* tile_m,
-                                         int32_t* tile_n, int32_t* k_slice) {
+moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int64_t M_rows, int32_t E,
+                                         int32_t* tile_m, int32_t* tile_n, int32_t* k_slice) {
   MOE_REQUIRE(tile_m && tile_n && k_slice, "null output pointer");
   MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS && M_rows >= 0, "bad M_rows or E");
   int m = 0, n = 0, ks = 0;
-  if (!moe::grouped_gemm_tile_shape(ab_dtype, epi == MOE_EPI_SILU_MUL, &m, &n, &ks))
+  if (!moe::grouped_gemm_tile_shape(ab_dtype, epi == MOE_EPI_SILU_MUL, M_rows, E, &m, &n, &ks))
     return fail(MOE_ERR_INVALID_ARG, "bad dtype %d", (int)ab_dtype);
   *tile_m = m;
   *tile_n = n;

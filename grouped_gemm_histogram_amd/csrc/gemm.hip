@@ -107,6 +107,20 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_TILE_FP8_SILU
 #define MOE_TILE_FP8_SILU 128, 256, 2, 4, 0, 3
 #endif
+// Decode-size bf16 launches (few routed rows per expert): 16-row tiles of 32 output
+// columns, one wave each, a deep LDS ring.  The weights stream through many small
+// tiles with more bytes in flight per CU, where 192-row tiles would leave most CUs
+// idle and most MFMA rows empty.
+#ifndef MOE_TILE_BF16_SILU_DEC
+#define MOE_TILE_BF16_SILU_DEC 16, 64, 1, 1, 0, 6
+#endif
+#ifndef MOE_TILE_BF16_NONE_DEC
+#define MOE_TILE_BF16_NONE_DEC 16, 32, 1, 1, 0, 6
+#endif
+// bf16 launches of at most this many rows per expert (M_rows <= this * E) use them
+#ifndef MOE_DECODE_ROWS_PER_EXPERT
+#define MOE_DECODE_ROWS_PER_EXPERT 8
+#endif
 #ifndef MOE_TILE_FP8_NONE
 #define MOE_TILE_FP8_NONE 128, 256, 2, 4, 0, 3
 #endif
@@ -142,6 +156,27 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, const void* base, uint32
 
 __device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most n slices of PER direct loads each are outstanding (n <= N; vmcnt
+// takes an immediate, so each count has its own instruction).  LGKM: also drain LDS reads.
+template <int PER, int N, bool LGKM>
+__device__ __forceinline__ void wait_slices(int n) {
+  if constexpr (N == 0) {
+    if constexpr (LGKM)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) {
+      if constexpr (LGKM)
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N * PER) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N * PER) : "memory");
+    } else {
+      wait_slices<PER, N - 1, LGKM>(n);
+    }
+  }
+}
+
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane(v);
 }
@@ -171,14 +206,14 @@ struct GemmCfg {
   static_assert(BM % (16 * WM) == 0 && BNB % (16 * WN) == 0, "tile/wave mismatch");
   static_assert(!SILU || kSNB % 2 == 0, "SiLU needs gate and up subtiles in every wave");
   static_assert((BM * 8) % kThreads == 0 && (BNB * 8) % kThreads == 0, "loader mismatch");
-  static_assert(kThreads / 8 % 16 == 0, "loader rows must keep the swizzle phase");
+  static_assert(kThreads / 8 % 8 == 0, "loader rows must keep the swizzle phase");
   static_assert(PF >= 0 && PF <= 2, "PF: 0 = direct-to-LDS loads, 1/2 = register prefetch depth");
   static constexpr int kNW = WM * WN;
   static constexpr int kDmaA = BM / 8 / kNW;       // direct loads per wave per slice (8 rows each)
   static constexpr int kDmaB = BNB / 8 / kNW;
   static_assert(PF != 0 || (BM % (8 * kNW) == 0 && BNB % (8 * kNW) == 0),
                 "direct loads need whole 8-row groups per wave");
-  static_assert(ST == 2 || (PF == 0 && ST == 3), "LDS stages: 2, or 3 with direct loads");
+  static_assert(ST == 2 || (PF == 0 && ST >= 3 && ST <= 8), "LDS stages: 2, or 3 to 8 with direct loads");
   static constexpr int kDmaPerSlice = kDmaA + kDmaB;
   static_assert(CT != CType::FP8 || (SILU && kBNOut == 128), "fp8 output needs 128-column tiles");
   // fp8 runs on direct loads only.  Each LDS stage then also holds the slice's
@@ -193,6 +228,7 @@ struct GemmCfg {
   static constexpr int kScaleBytes = kLdsScales ? kNW * 256 : 0;
   static constexpr int kStageBytes = kTileBytes + kScaleBytes;
   static constexpr int kDmaTotal = kDmaPerSlice + (kLdsScales ? 1 : 0);   // loads per wave per slice
+  static_assert(PF != 0 || (ST - 2) * kDmaTotal <= 63, "outstanding direct loads must fit vmcnt");
 };
 
 // Output column (within the wave's slab) held by MFMA row ii of subtile s.
@@ -585,11 +621,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           // MFMAs of step 1 (operands already in registers) cover the LDS reads of
           // the next slice's step 0 instead of the whole workgroup stalling on them.
           //
-          // Stage reuse: the loads of slice kt+2 land in the stage of slice kt-1.
-          // Every wave has finished reading slice kt-1 before barrier kt-1 (its reads
-          // are drained with lgkmcnt(0) there), and slice kt+2's loads are issued
-          // after it, in the body of slice kt.
-          static_assert(ST == 3, "the pipelined loop needs three LDS stages");
+          // ST stages, ST-1 slices in flight.  Stage reuse: the loads of slice
+          // kt+ST-1 land in the stage of slice kt-1.  Every wave has finished reading
+          // slice kt-1 before barrier kt-1 (its reads are drained with lgkmcnt(0)
+          // there), and slice kt+ST-1's loads are issued after it, in the body of
+          // slice kt.
           constexpr bool FULL = decltype(full_tag)::value;
           bool live[SM];
 #pragma unroll
@@ -638,17 +674,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           }
           uint4 fa0[SM], fw0[SNB], fa1[SM], fw1[SNB];
           if (pre_here) {
-            // slices 0 and 1 were issued before the previous tile's epilogue, whose
+            // the first slices were issued before the previous tile's epilogue, whose
             // stores follow them on the counter: wait for everything
             wait_all_vm();
           } else {
-            issue(0, st);
-            if (KT > 1) {
-              issue(1, st == 2 ? 0 : st + 1);
-              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
-            } else {
-              wait_all_vm();
-            }
+            const int npro = min(ST - 1, KT);
+            for (int s2 = 0; s2 < npro; ++s2) issue(s2, (st + s2) % ST);
+            wait_slices<Cfg::kDmaPerSlice, ST - 2, false>(npro - 1);   // slice 0 has landed
           }
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
@@ -663,25 +695,22 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             const uint32_t keep1 = (tail && kt * kSliceBytes + (4 + g) * 16 >= k_bytes) ? 0u : ~0u;
             read_step(st, 1, fa1, fw1);
             __builtin_amdgcn_sched_barrier(0);
-            const bool more = kt + 2 < KT;
-            const int st2 = (st == 0) ? 2 : st - 1;   // stage of slice kt+2
+            const bool more = kt + ST - 1 < KT;
+            const int stn = (st == 0) ? ST - 1 : st - 1;   // stage of slice kt+ST-1 (= of kt-1)
 #pragma unroll
             for (int t = 0; t < SM; ++t) {
               mma_row(t, fa0, fw0, keep0);
               if (!LAST && more) {
 #pragma unroll
                 for (int j = 0; j < Cfg::kDmaPerSlice; ++j)
-                  if (j * SM / Cfg::kDmaPerSlice == t) issue_one(j, kt + 2, st2);
+                  if (j * SM / Cfg::kDmaPerSlice == t) issue_one(j, kt + ST - 1, stn);
               }
               __builtin_amdgcn_sched_barrier(0);
             }
-            const int st1 = (st == 2) ? 0 : st + 1;
+            const int st1 = (st == ST - 1) ? 0 : st + 1;
             if constexpr (!LAST) {
-              // slice kt+1 has landed once only slice kt+2's loads are outstanding
-              if (more)
-                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::kDmaPerSlice) : "memory");
-              else
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+              // slice kt+1 has landed once only the slices after it are outstanding
+              wait_slices<Cfg::kDmaPerSlice, ST - 2, true>(min(ST - 2, KT - 2 - kt));
               __builtin_amdgcn_s_barrier();
               asm volatile("" ::: "memory");
               read_step(st1, 0, fa0, fw0);
@@ -694,16 +723,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           };
           for (int kt = 0; kt + 1 < KT; ++kt) body(kt, std::integral_constant<bool, false>{});
           body(KT - 1, std::integral_constant<bool, true>{});
-          // Cross-tile prefetch: the next tile's first two slices are issued now, before
+          // Cross-tile prefetch: the next tile's first ST-1 slices are issued now, before
           // this tile's epilogue, so their latency overlaps it.  They land in the stages
-          // of this workgroup's slices gk+KT-3 and gk+KT-2 (global count), which every
-          // wave finished reading before that slice's barrier, or, for a slice that is
-          // the last of its tile, before the next tile's first barrier.
+          // of this workgroup's slices gk+KT-ST .. gk+KT-2 (global count), never in that
+          // of the slice just read; every wave finished reading each of them before that
+          // slice's barrier, or, for a slice that is the last of its tile, before the
+          // next tile's first barrier.
           if (has_next) {
             if (nx.KT > 0) {
               const uint8_t* na = uniform_ptr(nx.a_src);
               const uint8_t* nb = uniform_ptr(nx.b_exp);
-              for (int s2 = 0; s2 < 2 && s2 < nx.KT; ++s2) {
+              for (int s2 = 0; s2 < ST - 1 && s2 < nx.KT; ++s2) {
                 const uint32_t o = min((uint32_t)(s2 * kSliceBytes) + cc, (uint32_t)(nx.k_bytes - 16));
                 const uint32_t sb = lds0 + (uint32_t)((gk + KT + s2) % ST) * Cfg::kStageBytes;
 #pragma unroll
@@ -1044,12 +1074,20 @@ struct TileOf {
 };
 }  // namespace
 
-bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice) {
+bool use_decode_tiles(long long M_rows, int E) {
+  return M_rows <= (long long)MOE_DECODE_ROWS_PER_EXPERT * E;
+}
+
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, int* tile_m, int* tile_n,
+                             int* k_slice) {
   if (ab_dtype == 1) {
+    const bool dec = use_decode_tiles(M_rows, E);
     using T1 = TileOf<MOE_TILE_BF16_SILU>;
     using T0 = TileOf<MOE_TILE_BF16_NONE>;
-    *tile_m = silu ? T1::kM : T0::kM;
-    *tile_n = silu ? T1::kN : T0::kN;
+    using D1 = TileOf<MOE_TILE_BF16_SILU_DEC>;
+    using D0 = TileOf<MOE_TILE_BF16_NONE_DEC>;
+    *tile_m = dec ? (silu ? D1::kM : D0::kM) : (silu ? T1::kM : T0::kM);
+    *tile_n = dec ? (silu ? D1::kN : D0::kN) : (silu ? T1::kN : T0::kN);
     *k_slice = kSliceBytes / 2;
   } else if (ab_dtype == 0) {
     *tile_m = 64;
@@ -1091,6 +1129,14 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
+  if (p.ab_dtype == 1 && !p.koff && use_decode_tiles(p.M_rows, p.E)) {
+    if (p.silu) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
+    }
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE_DEC>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE_DEC>(a, stream);
+  }
   if (p.ab_dtype == 1) {
     if (p.silu) {
       if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU>(a, stream);

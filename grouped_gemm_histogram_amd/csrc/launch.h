@@ -48,7 +48,8 @@ struct GemmLaunch {
   long long a_total = 0;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
-bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int* tile_m, int* tile_n, int* k_slice);
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, int* tile_m, int* tile_n,
+                             int* k_slice);
 
 // backward steps (backward.hip)
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);

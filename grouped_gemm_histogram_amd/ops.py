@@ -170,11 +170,12 @@ def quantize_rows(x: torch.Tensor):
     return xq, xs
 
 
-def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str = "none"):
-    """(tile rows, tile weight rows, K elements per slice) of moe_grouped_gemm for a dtype/epilogue."""
+def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str, M_rows: int, E: int):
+    """(tile rows, tile weight rows, K elements per slice) of moe_grouped_gemm for a dtype, epilogue
+    and launch size (M_rows product rows over E experts)."""
     m, n, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(load().grouped_gemm_tile_shape(_DT[dtype], _EPI[epilogue], ctypes.byref(m), ctypes.byref(n),
-                                          ctypes.byref(k)))
+    _check(load().grouped_gemm_tile_shape(_DT[dtype], _EPI[epilogue], M_rows, E, ctypes.byref(m),
+                                          ctypes.byref(n), ctypes.byref(k)))
     return m.value, n.value, k.value
 
 

@@ -106,6 +106,26 @@ def test_backward_small_layers(name):
         assert np.all(np32(gr.dw13)[e] == 0) and np.all(np32(gr.dw2)[e] == 0)
 
 
+def test_backward_decode_size():
+    """A few tokens (at most 8 routed rows per expert): the M-grouped GEMMs take the decode tiles."""
+    cfg = small_variant(get_config("gptoss20b_bf16"), 6).replace(H=712, I=456)
+    say(f"backward decode-size T={cfg.T} R={cfg.R}")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dout = _dout(cfg.T, cfg.H, 27)
+    gr = _gpu_backward(inp, w, off, sr, rp, dout)
+    ref = obwd.backward(inp.x.float().cpu().numpy(), ids, w, _weights(inp), dout.float().numpy())
+    errs = {"dx": row_rel_err(np32(gr.dx), ref["dx"]),
+            "dw13": _per_expert(np32(gr.dw13), ref["dw13"]),
+            "dw2": _per_expert(np32(gr.dw2), ref["dw2"]),
+            "dw": row_rel_err(np32(gr.dtopk_weights).reshape(1, -1), ref["dw"].reshape(1, -1))}
+    say(f"  errors {errs}")
+    for key, err in errs.items():
+        assert err <= TOL, (key, err)
+    for e in np.flatnonzero(np.diff(off) == 0):
+        assert np.all(np32(gr.dw13)[e] == 0) and np.all(np32(gr.dw2)[e] == 0)
+
+
 def test_backward_bf16_grads_and_determinism():
     cfg = _cfg("gptoss20b_bf16")
     inp = generate(cfg, DEV)

@@ -214,6 +214,10 @@ GEMM_CASES = [
     ("bf16", 500, 480, 4, 2 * 104, 192, "silu_mul"),
     ("f32", 500, 420, 5, 2 * 100, 96, "silu_mul"),
     ("f32", 500, 500, 5, 132, 68, "none"),
+    # decode-size launches (at most 8 rows per expert): 16-row tiles, ragged N and K tails
+    ("bf16", 40, 40, 6, 400, 200, "silu_mul"),
+    ("bf16", 60, 55, 8, 136, 72, "none"),
+    ("bf16", 16, 9, 4, 2 * 1408, 384, "silu_mul"),
 ]
 
 
@@ -347,6 +351,8 @@ GATHER_CASES = [
     ("bf16", 64, 4, 2, 0, 128, 64, "silu_mul"),
     ("bf16", 700, 3, 1, -1, 400, 200, "silu_mul"),
     ("f32", 200, 6, 3, 450, 2 * 100, 96, "silu_mul"),
+    ("bf16", 5, 16, 4, -1, 2 * 456, 712, "silu_mul"),         # decode tiles
+    ("bf16", 30, 8, 2, 50, 384, 264, "none"),                 # decode tiles, K tail
     ("fp8", 200, 8, 4, 700, 512, 384, "silu_mul"),
     ("fp8", 150, 5, 2, -1, 384, 256, "none"),
 ]
@@ -400,10 +406,11 @@ def test_grouped_gemm_gather(dt, T, E, k, nv, N, K, epi):
     assert torch.equal(C.cpu().view(idt), C2.cpu().view(idt))
 
 
-def test_grouped_gemm_gather_exact_bf16():
-    say("gather gemm exact bf16")
-    T, E, k, N, K = 400, 6, 3, 256, 384
-    ids, w, off, sr, rp = _routing(T, E, k, 1100, 31)
+@pytest.mark.parametrize("T", [400, 16])
+def test_grouped_gemm_gather_exact_bf16(T):
+    say(f"gather gemm exact bf16 T={T}")
+    E, k, N, K = 6, 3, 256, 384
+    ids, w, off, sr, rp = _routing(T, E, k, T * k - 20, 31)
     gen = torch.Generator().manual_seed(32)
     A = torch.randint(-4, 5, (T, K), generator=gen).to(torch.bfloat16)
     B = torch.randint(-4, 5, (E, N, K), generator=gen).to(torch.bfloat16)

@@ -129,6 +129,35 @@ def test_layer_top1_unit_weight_is_expert_ffn():
     assert row_rel_err(np32(out), ref) <= TOL["bf16"]
 
 
+# ------------------------------------------------------------------------------ decode sizes
+
+DECODE = [
+    # workload, T, width overrides; at most 8 routed rows per expert -> 16-row decode tiles
+    ("gptoss20b_bf16", 1, {}), ("gptoss20b_bf16", 3, {}), ("gptoss20b_bf16", 16, {}),
+    ("gptoss20b_bf16", 64, {}),
+    # skewed loads (per-expert logit bias): one expert spans several 16-row tiles
+    ("mixtral8x7b_bf16", 32, dict(H=384, I=1408)),
+]
+
+
+@pytest.mark.parametrize("name,T,kw", DECODE)
+def test_layer_decode_sizes(name, T, kw):
+    import grouped_gemm_histogram_amd as g
+    cfg = small_variant(get_config(name), T, "_decode").replace(**kw)
+    say(f"layer decode {cfg.name}: T={T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+    assert g.grouped_gemm_tile_shape(torch.bfloat16, "silu_mul", cfg.R, cfg.E)[0] == 16
+    inp = generate(cfg, DEV)
+    out, aux = _run(inp)
+    ref = olayer.forward(np32(inp.x), inp.logits.cpu().numpy(), _weights_host(inp), cfg.k,
+                         cfg.num_valid_rows, cfg.renormalize)
+    _check_routing(aux, ref)
+    if kw:
+        assert np.diff(ref["offsets"]).max() > 16          # the skew case covers several m-tiles
+    err = row_rel_err(np32(out), ref["out"])
+    say(f"  max row-relative error {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------------------ full size
 
 FULL = ["gptoss20b_bf16", "sweep_bf16_v16384", "sweep_bf16_v8192", "sweep_bf16_v2048",
