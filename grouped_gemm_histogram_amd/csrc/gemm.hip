@@ -107,19 +107,27 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_TILE_FP8_SILU
 #define MOE_TILE_FP8_SILU 128, 256, 2, 4, 0, 3
 #endif
-// Decode-size bf16 launches (few routed rows per expert): 16-row tiles of 32 output
-// columns, one wave each, a deep LDS ring.  The weights stream through many small
-// tiles with more bytes in flight per CU, where 192-row tiles would leave most CUs
-// idle and most MFMA rows empty.
+// Decode-size bf16 launches (few routed rows per expert): one-wave tiles of 16 rows
+// by 16 output columns (SiLU*up: 16 gate + 16 up weight rows) or 32 (no epilogue),
+// and an 8-stage LDS ring.  The weights stream through many small tiles with more
+// bytes in flight per CU, where 192-row tiles would leave most CUs idle and most MFMA
+// rows empty.  With at most 2 rows per expert the no-epilogue tiles narrow to 16
+// columns as well (twice the tiles; at more rows the wider tile is as fast).
 #ifndef MOE_TILE_BF16_SILU_DEC
-#define MOE_TILE_BF16_SILU_DEC 16, 64, 1, 1, 0, 6
+#define MOE_TILE_BF16_SILU_DEC 16, 32, 1, 1, 0, 8
 #endif
 #ifndef MOE_TILE_BF16_NONE_DEC
-#define MOE_TILE_BF16_NONE_DEC 16, 32, 1, 1, 0, 6
+#define MOE_TILE_BF16_NONE_DEC 16, 32, 1, 1, 0, 8
+#endif
+#ifndef MOE_TILE_BF16_NONE_DEC_NARROW
+#define MOE_TILE_BF16_NONE_DEC_NARROW 16, 16, 1, 1, 0, 8
 #endif
 // bf16 launches of at most this many rows per expert (M_rows <= this * E) use them
 #ifndef MOE_DECODE_ROWS_PER_EXPERT
 #define MOE_DECODE_ROWS_PER_EXPERT 8
+#endif
+#ifndef MOE_DECODE_NARROW_ROWS_PER_EXPERT
+#define MOE_DECODE_NARROW_ROWS_PER_EXPERT 2
 #endif
 #ifndef MOE_TILE_FP8_NONE
 #define MOE_TILE_FP8_NONE 128, 256, 2, 4, 0, 3
@@ -1077,17 +1085,22 @@ struct TileOf {
 bool use_decode_tiles(long long M_rows, int E) {
   return M_rows <= (long long)MOE_DECODE_ROWS_PER_EXPERT * E;
 }
+bool use_narrow_decode_tiles(long long M_rows, int E) {
+  return M_rows <= (long long)MOE_DECODE_NARROW_ROWS_PER_EXPERT * E;
+}
 
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, int* tile_m, int* tile_n,
                              int* k_slice) {
   if (ab_dtype == 1) {
     const bool dec = use_decode_tiles(M_rows, E);
+    const bool narrow = use_narrow_decode_tiles(M_rows, E);
     using T1 = TileOf<MOE_TILE_BF16_SILU>;
     using T0 = TileOf<MOE_TILE_BF16_NONE>;
     using D1 = TileOf<MOE_TILE_BF16_SILU_DEC>;
     using D0 = TileOf<MOE_TILE_BF16_NONE_DEC>;
-    *tile_m = dec ? (silu ? D1::kM : D0::kM) : (silu ? T1::kM : T0::kM);
-    *tile_n = dec ? (silu ? D1::kN : D0::kN) : (silu ? T1::kN : T0::kN);
+    using N0 = TileOf<MOE_TILE_BF16_NONE_DEC_NARROW>;
+    *tile_m = dec ? (silu ? D1::kM : (narrow ? N0::kM : D0::kM)) : (silu ? T1::kM : T0::kM);
+    *tile_n = dec ? (silu ? D1::kN : (narrow ? N0::kN : D0::kN)) : (silu ? T1::kN : T0::kN);
     *k_slice = kSliceBytes / 2;
   } else if (ab_dtype == 0) {
     *tile_m = 64;
@@ -1133,6 +1146,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
     if (p.silu) {
       if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
       return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
+    }
+    if (use_narrow_decode_tiles(p.M_rows, p.E)) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE_DEC_NARROW>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE_DEC_NARROW>(a, stream);
     }
     if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE_DEC>(a, stream);
     return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE_DEC>(a, stream);

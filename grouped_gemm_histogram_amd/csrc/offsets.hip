@@ -15,6 +15,7 @@
 //               row's rank among equal ids in the same 64 comes from ballots
 //               over the id bits (lanes with equal ids), so ties keep flat
 //               order without any atomic.
+// A launch of at most one chunk (decode sizes) runs all three in one workgroup.
 
 #include "device_common.h"
 #include "launch.h"
@@ -85,20 +86,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist
   }
 }
 
-// One wave per chunk.
-__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int R, int E,
-                                                     int id_bits,
-                                                     const int* __restrict__ chunk_base,
-                                                     int* __restrict__ sorted_rows,
-                                                     int* __restrict__ row_pos) {
-  __shared__ int cursor[kMaxBins];
-  const int nb = E + 1;
+// One wave places rows [r0, r1) (at most one chunk) in order; cursor[b] (LDS) holds the
+// next position of bin b and is advanced.
+__device__ __forceinline__ void scatter_rows(const int* __restrict__ ids, int r0, int r1, int E, int id_bits,
+                                             int* cursor, int* __restrict__ sorted_rows,
+                                             int* __restrict__ row_pos) {
   const int lane = lane_id();
-  for (int i = lane; i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i];
-  __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const int r0 = blockIdx.x * kChunk;
-  const int r1 = min(R, r0 + kChunk);
   // all of the chunk's ids are loaded up front (one round trip instead of one per step)
   constexpr int kSteps = kChunk / kWave;
   int keys[kSteps];
@@ -134,6 +128,49 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   }
 }
 
+// One wave per chunk.
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int R, int E,
+                                                     int id_bits,
+                                                     const int* __restrict__ chunk_base,
+                                                     int* __restrict__ sorted_rows,
+                                                     int* __restrict__ row_pos) {
+  __shared__ int cursor[kMaxBins];
+  const int nb = E + 1;
+  for (int i = lane_id(); i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i];
+  __syncthreads();
+  const int r0 = blockIdx.x * kChunk;
+  scatter_rows(ids, r0, min(R, r0 + kChunk), E, id_bits, cursor, sorted_rows, row_pos);
+}
+
+// R <= kChunk: histogram, bin scan and scatter in one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restrict__ ids, int R, int E,
+                                                              int id_bits, int* __restrict__ offsets,
+                                                              int* __restrict__ sorted_rows,
+                                                              int* __restrict__ row_pos) {
+  __shared__ int tot[2][kMaxBins + 1];
+  const int nb = E + 1;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) tot[0][b] = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&tot[0][bin_of(ids[r], E)], 1);
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the nb bin counts
+  int src = 0;
+  for (int d = 1; d < nb; d <<= 1) {
+    for (int b = threadIdx.x; b < nb; b += blockDim.x)
+      tot[src ^ 1][b] = tot[src][b] + (b >= d ? tot[src][b - d] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  // exclusive bases: offsets[b], and the scatter cursors (in the other buffer)
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const int base = (b == 0) ? 0 : tot[src][b - 1];
+    offsets[b] = base;
+    tot[src ^ 1][b] = base;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) scatter_rows(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
+}
+
 size_t build_offsets_workspace_bytes(long long R, int E) {
   const long long nchunks = (R + kChunk - 1) / kChunk;
   return (size_t)(nchunks > 0 ? nchunks : 1) * (size_t)(E + 1) * sizeof(int);
@@ -145,6 +182,11 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
   int* chunk_hist = static_cast<int*>(workspace);
   int id_bits = 1;
   while ((1 << id_bits) <= E) ++id_bits;   // bins 0..E need id_bits bits
+  if (nchunks <= 1) {
+    hipLaunchKernelGGL(offsets_single_kernel, dim3(1), dim3(1024), 0, stream, ids, R, E, id_bits, offsets,
+                       sorted_rows, row_pos);
+    return hipGetLastError();
+  }
   if (nchunks > 0)
     hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, chunk_hist);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E,

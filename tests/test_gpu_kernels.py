@@ -52,8 +52,9 @@ def test_route_topk(T, E, k, ties):
 
 # ------------------------------------------------------------------------------------ offsets
 
-OFFSET_CASES = [(1, 1), (100, 3), (1000, 8), (1025, 8), (4096, 129), (16384, 128), (65536, 256),
-                (70000, 1024), (5000, 1024), (3000, 1)]
+# R <= 1024 runs the single-workgroup kernel, larger R the three-kernel chunked path
+OFFSET_CASES = [(1, 1), (100, 3), (1000, 8), (1024, 32), (1024, 1024), (64, 1024), (700, 256),
+                (1025, 8), (4096, 129), (16384, 128), (65536, 256), (70000, 1024), (5000, 1024), (3000, 1)]
 
 
 @pytest.mark.parametrize("R,E", OFFSET_CASES)
@@ -73,9 +74,10 @@ def test_build_offsets(R, E):
 
 
 @pytest.mark.parametrize("pattern", ["one_expert", "all_sentinel", "one_hot", "last_expert"])
-def test_build_offsets_degenerate(pattern):
-    say(f"offsets degenerate {pattern}")
-    R, E = 5000, 64
+@pytest.mark.parametrize("R", [5000, 900])
+def test_build_offsets_degenerate(pattern, R):
+    say(f"offsets degenerate {pattern} R={R}")
+    E = 64
     if pattern == "one_expert":
         ids = np.full(R, 17, np.int32)
     elif pattern == "all_sentinel":
@@ -217,6 +219,7 @@ GEMM_CASES = [
     # decode-size launches (at most 8 rows per expert): 16-row tiles, ragged N and K tails
     ("bf16", 40, 40, 6, 400, 200, "silu_mul"),
     ("bf16", 60, 55, 8, 136, 72, "none"),
+    ("bf16", 12, 10, 8, 136, 72, "none"),                     # narrow decode tiles (<= 2 rows/expert)
     ("bf16", 16, 9, 4, 2 * 1408, 384, "silu_mul"),
 ]
 
