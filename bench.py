@@ -206,19 +206,21 @@ def time_decode(g, torch, cfg, inp, steps: int, tokens=(1, 8, 64)) -> list:
     launches take the 16-row decode tiles; the bound is streaming each touched expert's weights
     once, so the rate reported is touched-weight bytes per layer time against 8 TB/s."""
     res = []
-    esz = 4 if cfg.dtype == "f32" else 2
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
     for T in tokens:
         c = cfg.replace(T=T)
         x, lg = inp.x[:T].contiguous(), inp.logits[:T].contiguous()
         ws = torch.empty(g.forward_workspace_bytes(T, c.H, c.I, c.E, c.k, inp.w13.dtype), dtype=torch.uint8,
                          device=x.device)
         out = torch.empty(T, c.H, dtype=inp.x.dtype, device=x.device)
-        _, aux = g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, out=out, workspace=ws, return_aux=True)
+        _, aux = g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, inp.w13_scale, inp.w2_scale, out=out,
+                           workspace=ws, return_aux=True)
         off = aux.offsets.cpu().tolist()
         touched = sum(1 for e in range(c.E) if off[e + 1] > off[e])
 
         def call():
-            g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, out=out, workspace=ws)
+            g.forward(x, lg, inp.w13, inp.w2, c.k, -1, c.renormalize, inp.w13_scale, inp.w2_scale, out=out,
+                      workspace=ws)
         warm(torch, call, 5, 0.3)
         ev = HipEvents(2)
         stream = torch.cuda.current_stream().cuda_stream
@@ -279,6 +281,8 @@ def main() -> int:
     ap.add_argument("--clamp-ab", action="store_true",
                     help="also time the staged layer with sentinel rows clamped onto the last expert")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-size layer timings")
+    ap.add_argument("--decode-only", type=int, default=0, metavar="T",
+                    help="time only the layer on the first T tokens (decode size) and print that line")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing moe_backward (bf16 workloads time it by default)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -303,6 +307,13 @@ def main() -> int:
     dev = "cuda:0"
     inp = generate(cfg, dev)
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    if args.decode_only:
+        a = torch.randn(4096, 4096, device=dev).to(torch.bfloat16)
+        warm(torch, lambda: torch.matmul(a, a), 1, args.warmup_seconds)
+        dec = time_decode(g, torch, cfg, inp, args.steps, tokens=(args.decode_only,))[0]
+        print(json.dumps({"metric": "MoE layer time at decode size", "workload": cfg.name, "dtype": cfg.dtype,
+                          "steps": max(args.steps, 50), **dec}))
+        return 0
     need = g.forward_workspace_bytes(T, H, I, E, k, inp.w13.dtype)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = torch.empty(T, H, dtype=torch.float32 if cfg.dtype == "f32" else torch.bfloat16, device=dev)

@@ -3,10 +3,13 @@
 //
 //   out[t] = sum_{j ascending, row valid} w[t*k+j] * y[row_pos[t*k+j]]
 //
-// One wave per token; each lane owns 16 bytes of the output row per step and
-// accumulates in fp32 in slot order (deterministic).  A row is valid iff its
-// permuted position is below offsets[E]; sentinel rows are never read, so a
-// token with no valid row stores exact zeros.
+// One wave per token and column range (a token's row is split over several waves
+// when there are few tokens, so that its loads are in flight at once); each lane
+// owns 16 bytes of the output row per step and accumulates in fp32 in slot order
+// (deterministic).  A row is valid iff its permuted position is below offsets[E];
+// sentinel rows are never read, so a token with no valid row stores exact zeros.
+
+#include <algorithm>
 
 #include "device_common.h"
 #include "launch.h"
@@ -24,13 +27,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const int* __restrict__ row_pos,
                                                       const float* __restrict__ weights,
                                                       const int* __restrict__ offsets, int E, int T,
-                                                      int H, int k, void* __restrict__ out_) {
+                                                      int H, int k, int nsplit, int cols,
+                                                      void* __restrict__ out_) {
   // Elements per lane per step: 8 for bf16 input (one 16-B load), 4 for f32.
   constexpr int EL = kBf16In ? 8 : 4;
   constexpr int kUnroll = 2;   // column steps whose row loads are in flight together
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = wv / nsplit;
   const int lane = lane_id();
   if (t >= T) return;
+  // columns [c_lo, c_hi) of the token (cols is a multiple of the 64-lane step)
+  const int c_lo = (wv - t * nsplit) * cols;
+  const int c_hi = min(H, c_lo + cols);
   const int V = offsets[E];
   // the token's k <= 16 slots, once: position (-1 if not a valid row) and weight of
   // slot j, made wave-uniform while every lane is still active
@@ -81,7 +89,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     }
   };
   constexpr int STEP = kWave * EL;
-  for (int cb = lane * EL; cb < H; cb += kUnroll * STEP) {
+  for (int cb = c_lo + lane * EL; cb < c_hi; cb += kUnroll * STEP) {
     float acc[kUnroll][EL];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
@@ -95,16 +103,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       float v[kUnroll][EL];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (cb + u * STEP < H) load_row(p, cb + u * STEP, v[u]);
+        if (cb + u * STEP < c_hi) load_row(p, cb + u * STEP, v[u]);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (cb + u * STEP < H)
+        if (cb + u * STEP < c_hi)
 #pragma unroll
           for (int i = 0; i < EL; ++i) acc[u][i] = fmaf(w, v[u][i], acc[u][i]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (cb + u * STEP < H) store_out(cb + u * STEP, acc[u]);
+      if (cb + u * STEP < c_hi) store_out(cb + u * STEP, acc[u]);
   }
 }
 
@@ -112,19 +120,26 @@ hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const 
                           const int* offsets, int E, int T, int H, int k, void* out, bool out_bf16,
                           hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid((T + 3) / 4), block(256);
+  // few tokens: split each row over up to ceil(1024 / T) waves of whole 64-lane steps
+  const int step = kWave * (y_bf16 ? 8 : 4);
+  const int steps = (H + step - 1) / step;
+  int nsplit = T >= 1024 ? 1 : std::min(steps, (1024 + T - 1) / T);
+  const int cols = (steps + nsplit - 1) / nsplit * step;
+  nsplit = (H + cols - 1) / cols;
+  const long long waves = (long long)T * nsplit;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   if (y_bf16 && out_bf16)
     hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, stream, y, row_pos, weights,
-                       offsets, E, T, H, k, out);
+                       offsets, E, T, H, k, nsplit, cols, out);
   else if (y_bf16)
     hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, stream, y, row_pos, weights,
-                       offsets, E, T, H, k, out);
+                       offsets, E, T, H, k, nsplit, cols, out);
   else if (out_bf16)
     hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, stream, y, row_pos, weights,
-                       offsets, E, T, H, k, out);
+                       offsets, E, T, H, k, nsplit, cols, out);
   else
     hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, stream, y, row_pos, weights,
-                       offsets, E, T, H, k, out);
+                       offsets, E, T, H, k, nsplit, cols, out);
   return hipGetLastError();
 }
 

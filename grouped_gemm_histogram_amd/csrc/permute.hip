@@ -4,9 +4,10 @@
 // transformers PR #45621 write-up, section 1, loads as fp8_act_quant /
 // per_token_cast_to_fp8).
 //
-// One wave per permuted row; 16-byte loads and stores, so each row moves as
-// coalesced 1 KiB wave transactions.  Positions at or past offsets[E] (the
-// sentinel tail) are skipped without touching memory.
+// One wave per permuted row (quantisation: per row and range of 512-channel
+// steps, so that few rows still spread over many waves); 16-byte loads and
+// stores, so each row moves as coalesced 1 KiB wave transactions.  Positions at
+// or past offsets[E] (the sentinel tail) are skipped without touching memory.
 
 #include "device_common.h"
 #include "launch.h"
@@ -37,26 +38,31 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 }
 
 // bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [H/128, R]; H % 128 == 0.
-// Each 16-lane group of the wave owns one 128-channel group per step.  With
-// sorted_rows and offsets null, row p is token row p and all R = T rows are
-// written (the per-token quantisation alone, for a GEMM that gathers its rows).
+// Each 16-lane group of the wave owns one 128-channel group per step; a wave
+// covers units [u_lo, u_lo + units) of its row (8-channel units, a multiple of
+// 64).  With sorted_rows and offsets null, row p is token row p and all R = T
+// rows are written (the per-token quantisation alone, for a GEMM that gathers
+// its rows).
 __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restrict__ x, int T,
                                                             int H, int k, const int* __restrict__ sorted_rows,
                                                             const int* __restrict__ offsets, int E,
-                                                            int R, uint2* __restrict__ xq,
-                                                            float* __restrict__ xs) {
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                            int R, int nsplit, int units,
+                                                            uint2* __restrict__ xq, float* __restrict__ xs) {
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = wv / nsplit;
   const int lane = lane_id();
   if (p >= R || (offsets != nullptr && p >= offsets[E])) return;
   const int src = sorted_rows != nullptr ? sorted_rows[p] / k : p;
   if (src < 0 || src >= T) return;   // inconsistent permutation: leave the row unwritten
   const int n8 = H / 8;                       // 8-channel units per row
+  const int u_lo = (wv - p * nsplit) * units;
+  const int u_hi = min(n8, u_lo + units);
   const uint4* s = x + (size_t)src * n8;
   uint2* d = xq + (size_t)p * n8;
   float* sc = xs + p;                         // scales are block-major: [H/128, R]
-  for (int base = 0; base < n8; base += kWave) {
+  for (int base = u_lo; base < u_hi; base += kWave) {
     const int u = base + lane;
-    const bool active = u < n8;               // whole 16-lane groups, as H % 128 == 0
+    const bool active = u < u_hi;             // whole 16-lane groups, as H % 128 == 0
     float v[8];
     float amax = 0.0f;
     if (active) {
@@ -97,10 +103,16 @@ hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
                                 hipStream_t stream) {
-  if (R > 0)
-    hipLaunchKernelGGL(permute_quant_kernel, dim3((R + 3) / 4), dim3(256), 0, stream,
-                       static_cast<const uint4*>(x), T, H, k, sorted_rows, offsets, E, R,
-                       static_cast<uint2*>(xq), xs);
+  if (R <= 0) return hipSuccess;
+  // few rows: split each row over up to ceil(1024 / R) waves of whole 64-lane steps
+  const int steps = (H / 8 + kWave - 1) / kWave;
+  int nsplit = R >= 1024 ? 1 : (steps < (1024 + R - 1) / R ? steps : (1024 + R - 1) / R);
+  const int units = (steps + nsplit - 1) / nsplit * kWave;
+  nsplit = (H / 8 + units - 1) / units;
+  const long long waves = (long long)R * nsplit;
+  hipLaunchKernelGGL(permute_quant_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                     static_cast<const uint4*>(x), T, H, k, sorted_rows, offsets, E, R, nsplit, units,
+                     static_cast<uint2*>(xq), xs);
   return hipGetLastError();
 }
 
