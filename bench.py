@@ -374,7 +374,9 @@ def main() -> int:
     R = cfg.R
     pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none", R, E))
     # SiLU*up tiles hold tile_n/2 output columns: count them against N_out = I
-    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul", R, E)
+    # the fp8 layer's gate/up writes e4m3 h (f32 h at decode sizes, quantised after)
+    h_dt = torch.float8_e4m3fn if cfg.dtype == "fp8" and R > 8 * E else None
+    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul", R, E, h_dt)
     pred_gu = predicted_mfma_flops(offsets_host, R, I, H, (tm, tn // 2, ks)) * 2
 
     # The dominant kernel's bound: the larger of its MFMA time and its HBM time at peak.

@@ -47,7 +47,7 @@ SIGNATURES: dict[str, tuple] = {
     "moe_grouped_gemm_gather": (I32, [P, P, I64, P, I32, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P,
                                       P]),
     "moe_quantize_rows": (I32, [P, I64, I64, P, P, P]),
-    "moe_grouped_gemm_tile_shape": (I32, [I32, I32, I64, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
+    "moe_grouped_gemm_tile_shape": (I32, [I32, I32, I32, I64, I32, ctypes.POINTER(I32), ctypes.POINTER(I32),
                                           ctypes.POINTER(I32)]),
     "moe_unpermute_combine": (I32, [P, I32, P, P, P, I32, I64, I64, I32, P, I32, P]),
     "moe_forward_workspace": (SZ, [I64, I64, I64, I32, I32, I32]),

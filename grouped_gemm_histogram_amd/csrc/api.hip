@@ -57,7 +57,7 @@ moe_status_t check_experts(int32_t E, int32_t k) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct FwdLayout {
-  size_t ids, w, offsets, sorted, rowpos, offws, xp, xps, h, hs, y, total;
+  size_t ids, w, offsets, sorted, rowpos, offws, xp, xps, hf, h, hs, y, total;
 };
 
 FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dtype_t w_dtype) {
@@ -80,6 +80,8 @@ FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dt
   L.offws = take(moe::build_offsets_workspace_bytes(R, E));
   L.xp = take(fp8 ? T * H : 0);                     // fp8: quantised token rows
   L.xps = take(fp8 ? T * (H / 128) * 4 : 0);
+  // fp8 at decode sizes: the gate/up GEMM's f32 h, quantised in a second pass
+  L.hf = take(fp8 && moe::use_decode_tiles(R, E) ? R * I * 4 : 0);
   L.h = take(R * I * e_act);
   L.hs = take(fp8 ? R * (I / 128) * 4 : 0);
   L.y = take(R * H * e_y);
@@ -265,13 +267,15 @@ moe_status_t moe_quantize_rows(const void* x, int64_t T, int64_t H, void* xq, fl
                   "quantize_rows");
 }
 
-moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int64_t M_rows, int32_t E,
-                                         int32_t* tile_m, int32_t* tile_n, int32_t* k_slice) {
+moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, moe_dtype_t c_dtype,
+                                         int64_t M_rows, int32_t E, int32_t* tile_m, int32_t* tile_n,
+                                         int32_t* k_slice) {
   MOE_REQUIRE(tile_m && tile_n && k_slice, "null output pointer");
   MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
   MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS && M_rows >= 0, "bad M_rows or E");
   int m = 0, n = 0, ks = 0;
-  if (!moe::grouped_gemm_tile_shape(ab_dtype, epi == MOE_EPI_SILU_MUL, M_rows, E, &m, &n, &ks))
+  MOE_REQUIRE(valid_dtype(c_dtype), "bad c_dtype");
+  if (!moe::grouped_gemm_tile_shape(ab_dtype, epi == MOE_EPI_SILU_MUL, c_dtype, M_rows, E, &m, &n, &ks))
     return fail(MOE_ERR_INVALID_ARG, "bad dtype %d", (int)ab_dtype);
   *tile_m = m;
   *tile_n = n;
@@ -371,9 +375,21 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   // quantises each token once first
   if (fp8 && (s = moe_quantize_rows(x, T, H, ws + L.xp, xps, stream))) return s;
   if ((s = mark(3))) return s;
-  if ((s = moe_grouped_gemm_gather(fp8 ? ws + L.xp : x, xps, T, sorted, k, w13, w13_scales, w_dtype, offs,
-                                   E, R, 2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream)))
+  if (fp8 && moe::use_decode_tiles(R, E)) {
+    // decode sizes: the small tiles write f32 h (an e4m3 group spans several of them),
+    // quantised per row and 128 channels after, with the fused epilogue's arithmetic
+    float* hf = reinterpret_cast<float*>(ws + L.hf);
+    if ((s = moe_grouped_gemm_gather(ws + L.xp, xps, T, sorted, k, w13, w13_scales, w_dtype, offs, E, R,
+                                     2 * I, H, MOE_EPI_SILU_MUL, hf, MOE_F32, nullptr, stream)))
+      return s;
+    if ((s = launched(moe::launch_permute_quant(hf, (int)R, (int)I, 1, nullptr, nullptr, 0, (int)R, ws + L.h, hs,
+                                                as_stream(stream), true),
+                      "quantize h")))
+      return s;
+  } else if ((s = moe_grouped_gemm_gather(fp8 ? ws + L.xp : x, xps, T, sorted, k, w13, w13_scales, w_dtype,
+                                          offs, E, R, 2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream))) {
     return s;
+  }
   if ((s = mark(4))) return s;
   if ((s = moe_grouped_gemm(ws + L.h, hs, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
                             ws + L.y, ydt, nullptr, stream)))

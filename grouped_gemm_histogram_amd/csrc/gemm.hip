@@ -122,6 +122,17 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_TILE_BF16_NONE_DEC_NARROW
 #define MOE_TILE_BF16_NONE_DEC_NARROW 16, 16, 1, 1, 0, 8
 #endif
+// Decode-size fp8 tiles: 16 rows, two waves (one loads the tile's activation scales,
+// the other the weight block scales).  Gate/up: 16 gate + 16 up weight rows per wave,
+// 32 output columns (f32 or bf16 h: a 128-column e4m3 group spans four such tiles, so
+// h is quantised in a second pass); down: 64 output columns.  fp8 output (the fused
+// quantising epilogue) keeps the 128-column tiles.
+#ifndef MOE_TILE_FP8_SILU_DEC
+#define MOE_TILE_FP8_SILU_DEC 16, 64, 1, 2, 0, 6
+#endif
+#ifndef MOE_TILE_FP8_NONE_DEC
+#define MOE_TILE_FP8_NONE_DEC 16, 64, 1, 2, 0, 6
+#endif
 // bf16 launches of at most this many rows per expert (M_rows <= this * E) use them
 #ifndef MOE_DECODE_ROWS_PER_EXPERT
 #define MOE_DECODE_ROWS_PER_EXPERT 8
@@ -230,9 +241,9 @@ struct GemmCfg {
   // waves: the weight scales, read from the first of them).
   static_assert(AB != AbType::FP8 || PF == 0, "fp8 needs direct loads");
   static constexpr bool kLdsScales = AB == AbType::FP8;
-  static constexpr int kScaleWaves = BM / 64;
-  static_assert(!kLdsScales || (BM % 64 == 0 && kScaleWaves < kNW && 2 * WN <= 64),
-                "fp8 tiles: BM a multiple of 64 and a spare wave for the weight scales");
+  static constexpr int kScaleWaves = (BM + 63) / 64;   // a wave loads the scales of 64 rows
+  static_assert(!kLdsScales || ((BM % 64 == 0 || BM < 64) && kScaleWaves < kNW && 2 * WN <= 64),
+                "fp8 tiles: BM below 64 or a multiple of it, and a spare wave for the weight scales");
   static constexpr int kScaleBytes = kLdsScales ? kNW * 256 : 0;
   static constexpr int kStageBytes = kTileBytes + kScaleBytes;
   static constexpr int kDmaTotal = kDmaPerSlice + (kLdsScales ? 1 : 0);   // loads per wave per slice
@@ -764,7 +775,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           // bf16 loop: slice kt+2's loads go to the stage of slice kt-1 and are issued
           // after barrier kt-1.  Each 128-deep MFMA gives one K block's partial sums,
           // which are scaled by (activation scale x weight scale) into the accumulator.
-          static_assert(ST == 3, "the pipelined loop needs three LDS stages");
           static_assert(SNB % 2 == 0, "two column halves");
           constexpr int SH = SNB / 2;   // weight subtiles per half (SiLU: gate, then up)
           constexpr bool FULL = decltype(full_tag)::value;
@@ -837,12 +847,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           auto next_stage = [](int x) MOE_INLINE { return (x + 1 == ST) ? 0 : x + 1; };
           ASet A0, A1;
           i32x8 w0[SH], w1[SH];
-          issue(0, st);
-          if (KT > 1) {
-            issue(1, next_stage(st));
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Cfg::kDmaTotal) : "memory");
-          } else {
-            wait_all_vm();
+          {
+            const int npro = min(ST - 1, KT);
+            for (int s2 = 0; s2 < npro; ++s2) issue(s2, (st + s2) % ST);
+            wait_slices<Cfg::kDmaTotal, ST - 2, false>(npro - 1);   // slice 0 has landed
           }
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
@@ -852,24 +860,21 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             constexpr bool LAST = decltype(last_tag)::value;
             read_w(st, 1, w1);
             __builtin_amdgcn_sched_barrier(0);
-            const bool more = kt + 2 < KT;
-            const int st2 = (st == 0) ? ST - 1 : st - 1;   // stage of slice kt+2
+            const bool more = kt + ST - 1 < KT;
+            const int stn = (st == 0) ? ST - 1 : st - 1;   // stage of slice kt+ST-1 (= of kt-1)
             mma_half(0, cur, w0, [&](int t) MOE_INLINE {
               if (!LAST && more) {
 #pragma unroll
                 for (int j = 0; j < Cfg::kDmaTotal; ++j)
-                  if (j * SM / Cfg::kDmaTotal == t) issue_one(j, kt + 2, st2);
+                  if (j * SM / Cfg::kDmaTotal == t) issue_one(j, kt + ST - 1, stn);
               }
               __builtin_amdgcn_sched_barrier(0);
             });
             __builtin_amdgcn_sched_barrier(0);
             const int st1 = next_stage(st);
             if constexpr (!LAST) {
-              // slice kt+1 has landed once only slice kt+2's loads are outstanding
-              if (more)
-                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(Cfg::kDmaTotal) : "memory");
-              else
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+              // slice kt+1 has landed once only the slices after it are outstanding
+              wait_slices<Cfg::kDmaTotal, ST - 2, true>(min(ST - 2, KT - 2 - kt));
               __builtin_amdgcn_s_barrier();
               asm volatile("" ::: "memory");
               read_a(st1, nxt);
@@ -1089,8 +1094,8 @@ bool use_narrow_decode_tiles(long long M_rows, int E) {
   return M_rows <= (long long)MOE_DECODE_NARROW_ROWS_PER_EXPERT * E;
 }
 
-bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, int* tile_m, int* tile_n,
-                             int* k_slice) {
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,
+                             int* tile_n, int* k_slice) {
   if (ab_dtype == 1) {
     const bool dec = use_decode_tiles(M_rows, E);
     const bool narrow = use_narrow_decode_tiles(M_rows, E);
@@ -1107,10 +1112,13 @@ bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, i
     *tile_n = 64;
     *k_slice = kSliceBytes / 4;
   } else if (ab_dtype == 2) {
+    const bool dec = c_dtype != 2 && use_decode_tiles(M_rows, E);
     using T1 = TileOf<MOE_TILE_FP8_SILU>;
     using T0 = TileOf<MOE_TILE_FP8_NONE>;
-    *tile_m = silu ? T1::kM : T0::kM;
-    *tile_n = silu ? T1::kN : T0::kN;
+    using D1 = TileOf<MOE_TILE_FP8_SILU_DEC>;
+    using D0 = TileOf<MOE_TILE_FP8_NONE_DEC>;
+    *tile_m = dec ? (silu ? D1::kM : D0::kM) : (silu ? T1::kM : T0::kM);
+    *tile_n = dec ? (silu ? D1::kN : D0::kN) : (silu ? T1::kN : T0::kN);
     *k_slice = kSliceBytes;
   } else {
     return false;
@@ -1171,6 +1179,14 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
     return launch_cfg<AbType::F32, CType::F32, false, 64, 64, 2, 2, 1, 2>(a, stream);
   }
   // fp8 operands
+  if (!p.koff && p.c_dtype != 2 && use_decode_tiles(p.M_rows, p.E)) {
+    if (p.silu) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, true, MOE_TILE_FP8_SILU_DEC>(a, stream);
+      return launch_cfg<AbType::FP8, CType::F32, true, MOE_TILE_FP8_SILU_DEC>(a, stream);
+    }
+    if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, false, MOE_TILE_FP8_NONE_DEC>(a, stream);
+    return launch_cfg<AbType::FP8, CType::F32, false, MOE_TILE_FP8_NONE_DEC>(a, stream);
+  }
   if (p.silu) {
     if (p.c_dtype == 2) return launch_cfg<AbType::FP8, CType::FP8, true, MOE_TILE_FP8_SILU>(a, stream);
     if (p.c_dtype == 1) return launch_cfg<AbType::FP8, CType::BF16, true, MOE_TILE_FP8_SILU>(a, stream);

@@ -16,10 +16,10 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
 
 hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
                                const int* offsets, int E, int R, void* xp, hipStream_t stream);
-// sorted_rows and offsets null: row p of xq is token row p, R = T rows
+// sorted_rows and offsets null: row p of xq is token row p, R = T rows; f32_in: x is f32
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
-                                hipStream_t stream);
+                                hipStream_t stream, bool f32_in = false);
 
 struct GemmLaunch {
   const void* A;
@@ -48,8 +48,10 @@ struct GemmLaunch {
   long long a_total = 0;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
-bool grouped_gemm_tile_shape(int ab_dtype, bool silu, long long M_rows, int E, int* tile_m, int* tile_n,
-                             int* k_slice);
+bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,
+                             int* tile_n, int* k_slice);
+// launches of at most 8 rows per expert take the decode tiles (bf16; fp8 with bf16/f32 output)
+bool use_decode_tiles(long long M_rows, int E);
 
 // backward steps (backward.hip)
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);

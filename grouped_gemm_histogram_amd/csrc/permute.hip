@@ -37,13 +37,14 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   for (; c < n16; c += kWave) d[c] = s[c];
 }
 
-// bf16 x [T, H] -> e4m3 codes xq [R, H] + scales xs [H/128, R]; H % 128 == 0.
+// bf16 (F32IN: f32) x [T, H] -> e4m3 codes xq [R, H] + scales xs [H/128, R]; H % 128 == 0.
 // Each 16-lane group of the wave owns one 128-channel group per step; a wave
 // covers units [u_lo, u_lo + units) of its row (8-channel units, a multiple of
 // 64).  With sorted_rows and offsets null, row p is token row p and all R = T
 // rows are written (the per-token quantisation alone, for a GEMM that gathers
 // its rows).
-__global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restrict__ x, int T,
+template <bool F32IN>
+__global__ __launch_bounds__(256) void permute_quant_kernel(const void* __restrict__ x_, int T,
                                                             int H, int k, const int* __restrict__ sorted_rows,
                                                             const int* __restrict__ offsets, int E,
                                                             int R, int nsplit, int units,
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restr
   const int n8 = H / 8;                       // 8-channel units per row
   const int u_lo = (wv - p * nsplit) * units;
   const int u_hi = min(n8, u_lo + units);
-  const uint4* s = x + (size_t)src * n8;
+  const uint4* s = static_cast<const uint4*>(x_) + (size_t)src * n8 * (F32IN ? 2 : 1);
   uint2* d = xq + (size_t)p * n8;
   float* sc = xs + p;                         // scales are block-major: [H/128, R]
   for (int base = u_lo; base < u_hi; base += kWave) {
@@ -66,12 +67,18 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const uint4* __restr
     float v[8];
     float amax = 0.0f;
     if (active) {
-      const uint4 raw = s[u];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      if constexpr (F32IN) {
+        const float4 a = __builtin_bit_cast(float4, s[2 * u]), b = __builtin_bit_cast(float4, s[2 * u + 1]);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      } else {
+        const uint4 raw = s[u];
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-        v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+          v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -102,7 +109,7 @@ hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const
 
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool f32_in) {
   if (R <= 0) return hipSuccess;
   // few rows: split each row over up to ceil(1024 / R) waves of whole 64-lane steps
   const int steps = (H / 8 + kWave - 1) / kWave;
@@ -110,9 +117,12 @@ hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* s
   const int units = (steps + nsplit - 1) / nsplit * kWave;
   nsplit = (H / 8 + units - 1) / units;
   const long long waves = (long long)R * nsplit;
-  hipLaunchKernelGGL(permute_quant_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
-                     static_cast<const uint4*>(x), T, H, k, sorted_rows, offsets, E, R, nsplit, units,
-                     static_cast<uint2*>(xq), xs);
+  if (f32_in)
+    hipLaunchKernelGGL(permute_quant_kernel<true>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x,
+                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs);
+  else
+    hipLaunchKernelGGL(permute_quant_kernel<false>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x,
+                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs);
   return hipGetLastError();
 }
 

@@ -170,12 +170,15 @@ def quantize_rows(x: torch.Tensor):
     return xq, xs
 
 
-def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str, M_rows: int, E: int):
-    """(tile rows, tile weight rows, K elements per slice) of moe_grouped_gemm for a dtype, epilogue
-    and launch size (M_rows product rows over E experts)."""
+def grouped_gemm_tile_shape(dtype: torch.dtype, epilogue: str, M_rows: int, E: int,
+                            out_dtype: Optional[torch.dtype] = None):
+    """(tile rows, tile weight rows, K elements per slice) of moe_grouped_gemm for a dtype, epilogue,
+    launch size (M_rows product rows over E experts) and output dtype (default: bf16 for fp8
+    operands, else the operand dtype)."""
+    out_dtype = out_dtype or (torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype)
     m, n, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(load().grouped_gemm_tile_shape(_DT[dtype], _EPI[epilogue], M_rows, E, ctypes.byref(m),
-                                          ctypes.byref(n), ctypes.byref(k)))
+    _check(load().grouped_gemm_tile_shape(_DT[dtype], _EPI[epilogue], _DT[out_dtype], M_rows, E,
+                                          ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)))
     return m.value, n.value, k.value
 
 

@@ -208,16 +208,18 @@ moe_status_t moe_quantize_rows(const void* x, int64_t T, int64_t H, void* xq, fl
 
 /*
  * moe_grouped_gemm_tile_shape -- the tile moe_grouped_gemm (and _gather) uses
- * for a dtype, epilogue and launch size (M_rows product rows over E experts;
- * bf16 launches with few rows per expert -- decode sizes -- take small tiles):
+ * for an operand dtype, epilogue, output dtype and launch size (M_rows product
+ * rows over E experts; launches with at most 8 rows per expert -- decode sizes --
+ * take small tiles, except fp8 launches with e4m3 output):
  * *tile_m activation rows by *tile_n weight rows (SiLU*up tiles hold tile_n/2
  * gate and tile_n/2 up rows), *k_slice elements of K per step.  Lets a caller
  * predict the MFMA work from offsets: each expert segment of M_e rows is
  * covered by ceil(M_e / tile_m) tiles in M, each computing 16 * ceil(rows / 16)
  * rows.  Returns MOE_ERR_INVALID_ARG for bad enums, sizes or null outputs.
  */
-moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, int64_t M_rows, int32_t E,
-                                         int32_t* tile_m, int32_t* tile_n, int32_t* k_slice);
+moe_status_t moe_grouped_gemm_tile_shape(moe_dtype_t ab_dtype, moe_epilogue_t epi, moe_dtype_t c_dtype,
+                                         int64_t M_rows, int32_t E, int32_t* tile_m, int32_t* tile_n,
+                                         int32_t* k_slice);
 
 /*
  * moe_unpermute_combine -- back to token order, scaled by the routing

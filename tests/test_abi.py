@@ -52,18 +52,21 @@ def test_version_and_strings(lib):
 
 def test_tile_shape_query(lib):
     m, n, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    shape = lambda dt, epi, M, E: (lib.grouped_gemm_tile_shape(dt, epi, M, E, ctypes.byref(m), ctypes.byref(n),
-                                                               ctypes.byref(k)), m.value, n.value, k.value)
+    shape = lambda dt, epi, M, E, c=1: (lib.grouped_gemm_tile_shape(dt, epi, c, M, E, ctypes.byref(m),
+                                                                    ctypes.byref(n), ctypes.byref(k)),
+                                        m.value, n.value, k.value)
     for dt in (0, 1, 2):
         for epi in (0, 1):
             for M in (16384, 4):
                 st, tm, tn, ks = shape(dt, epi, M, 32)
                 assert st == 0 and tm % 16 == 0 and tn % 16 == 0 and ks * (4, 2, 1)[dt] == 128
-    # bf16 launches with few rows per expert (decode sizes) take smaller tiles
+    # launches with few rows per expert (decode sizes) take smaller tiles; fp8 output keeps 128 columns
     assert shape(1, 1, 4, 32)[1] < shape(1, 1, 16384, 32)[1]
-    assert lib.grouped_gemm_tile_shape(7, 0, 64, 8, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
-    assert lib.grouped_gemm_tile_shape(1, 0, 64, 8, None, ctypes.byref(n), ctypes.byref(k)) == 1
-    assert lib.grouped_gemm_tile_shape(1, 0, 64, 0, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
+    assert shape(2, 1, 4, 32)[1] < shape(2, 1, 16384, 32)[1]
+    assert shape(2, 1, 4, 32, c=2)[1] == shape(2, 1, 16384, 32, c=2)[1]
+    assert lib.grouped_gemm_tile_shape(7, 0, 1, 64, 8, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
+    assert lib.grouped_gemm_tile_shape(1, 0, 1, 64, 8, None, ctypes.byref(n), ctypes.byref(k)) == 1
+    assert lib.grouped_gemm_tile_shape(1, 0, 1, 64, 0, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
 
 
 def test_host_validation(lib):

@@ -289,13 +289,18 @@ def _u8_to_fp8(a):
     (600, 600, 5, 512, 384, "silu_mul", "bf16"),
     (600, 480, 7, 384, 256, "none", "bf16"),
     (300, 0, 3, 256, 128, "silu_mul", "fp8"),
+    # decode sizes (at most 8 rows per expert): 16-row tiles; fp8 output keeps 128-column tiles
+    (40, 40, 6, 512, 384, "silu_mul", "bf16"),
+    (40, 33, 6, 512, 384, "silu_mul", "f32"),
+    (30, 25, 5, 384, 256, "none", "bf16"),
+    (20, 18, 4, 512, 256, "silu_mul", "fp8"),
 ])
 def test_grouped_gemm_fp8(M, V, E, N, K, epi, out):
     say(f"gemm fp8 M={M} V={V} E={E} N={N} K={K} {epi} -> {out}")
     aq, as_, bq, bs = _fp8_operands(M, E, N, K, M + N)
     off = _segments(M, E, V, E + 7)
     g = ops()
-    odt = torch.float8_e4m3fn if out == "fp8" else torch.bfloat16
+    odt = {"fp8": torch.float8_e4m3fn, "bf16": torch.bfloat16, "f32": torch.float32}[out]
     n_out = N // 2 if epi == "silu_mul" else N
     C = torch.full((M, n_out), float("nan"), dtype=torch.float32, device=DEV).to(odt)
     res = g.grouped_gemm(_u8_to_fp8(aq), _u8_to_fp8(bq), torch.from_numpy(off).to(DEV), epi,
