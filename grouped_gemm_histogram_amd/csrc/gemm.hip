@@ -20,11 +20,16 @@
 //    remapped so that consecutive tiles go to workgroups of the same XCD
 //    (workgroup w is dispatched to XCD w % 8): tiles that share a weight
 //    panel and an activation panel meet in that XCD's L2.
-//  * K is walked in 128-byte slices (64 bf16 / 32 f32 / 128 e4m3 per row),
-//    double-buffered in LDS through registers: the next slice's global loads
-//    are in flight while the current one feeds the MFMAs.  Each LDS row is
-//    128 bytes = eight 16-byte chunks stored XOR-swizzled, so that the
-//    16 rows read by one MFMA operand fetch hit distinct banks.
+//  * K is walked in 128-byte slices (64 bf16 / 32 f32 / 128 e4m3 per row).
+//    bf16 and e4m3 tiles fill a ring of ST LDS stages with direct global->LDS
+//    loads, ST-1 slices in flight while one feeds the MFMAs; f32 tiles (the
+//    reference-precision configuration) double-buffer through registers.  Each
+//    LDS row is 128 bytes = eight 16-byte chunks stored XOR-swizzled, so that
+//    the 16 rows read by one MFMA operand fetch hit distinct banks.
+//  * Modes: A read directly or gathered through a row map (token rows read
+//    through the permutation); K-grouped (weight gradients: each expert's own K
+//    range, every expert's full output); decode-size tiles (16 rows, one or two
+//    waves, deep rings) for launches with at most 8 rows per expert.
 //  * MFMA operand roles are swapped: weight rows are the 16-row src0 operand
 //    and activation rows the src1 operand, so each lane's results are output
 //    columns of one activation row.  Inside each wave the weight rows are
@@ -555,7 +560,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
     };
 
-    // ---- K loop: LDS double buffer fed from registers, PF slices of loads in flight
+    // ---- K loop: direct loads into an ST-stage LDS ring (PF = 0), or an LDS double buffer
+    //      fed from registers with PF slices of loads in flight (PF = 1, 2)
     auto k_loop = [&](auto full_tag) MOE_INLINE {
       if constexpr (PF == 0) {
         // Direct global->LDS loads into ST LDS stages, ST-1 slices in flight.  The
