@@ -201,6 +201,33 @@ def warm(torch, call, at_least: int, seconds: float) -> int:
     return n
 
 
+def time_permute(g, torch, cfg, inp, aux, steps: int) -> dict:
+    """moe_permute on its own (the scatter step; the layer's gate/up GEMM reads token rows
+    through the permutation instead): V rows read and written, HIP events on its stream."""
+    fp8 = cfg.dtype == "fp8"
+    out_dt = torch.float8_e4m3fn if fp8 else inp.x.dtype
+    xp = torch.empty(cfg.R, cfg.H, dtype=out_dt, device=inp.x.device)
+    xs = torch.empty(cfg.H // 128, cfg.R, dtype=torch.float32, device=inp.x.device) if fp8 else None
+
+    def call():
+        g.permute(inp.x, aux.sorted_rows, aux.offsets, cfg.k, out_dtype=out_dt, out=xp, out_scales=xs)
+    warm(torch, call, 5, 0.2)
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    n = max(steps, 20)
+    ev.record(0, stream)
+    for _ in range(n):
+        call()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    us = ev.ms(0, 1) / n * 1e3
+    ev.close()
+    esz = inp.x.element_size()
+    V = cfg.V
+    moved = V * cfg.H * esz + (V * cfg.H + V * (cfg.H // 128) * 4 if fp8 else V * cfg.H * esz)
+    return {"us": us, "bytes": moved, "gbs": moved / (us * 1e-6) / 1e9}
+
+
 def time_decode(g, torch, cfg, inp, steps: int, tokens=(1, 8, 64)) -> list:
     """The layer at decode sizes on the same weights: the first T tokens of the batch.  These
     launches take the 16-row decode tiles; the bound is streaming each touched expert's weights
@@ -347,6 +374,8 @@ def main() -> int:
     device_ms = sum(ev.ms(i * (nst + 1), i * (nst + 1) + nst) for i in range(args.steps)) / args.steps
     ev.close()
 
+    permute = time_permute(g, torch, cfg, inp, aux, args.steps)
+
     decode = None
     if cfg.dtype == "bf16" and not args.no_decode:
         decode = time_decode(g, torch, cfg, inp, args.steps)
@@ -415,6 +444,7 @@ def main() -> int:
         "stage_ms": stage_ms,
         "device_ms_per_step": device_ms,
         "combine_gbs": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
+        "permute_standalone": permute,
         "valid_rows_offsets_last": offsets_host[-1],
         "predicted_mfma_flops": {"gemm_gate_up": pred_gu, "gemm_down": pred_dn},
         "roofline": roofline,

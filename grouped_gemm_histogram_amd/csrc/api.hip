@@ -488,11 +488,12 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
   const int gdt = grad_dtype;
   auto gemm = [&](const void* A, const void* B, long long M, long long N, long long K, void* C, int cdt,
                   const int* kof, long long lda, long long ldb, int nE, const int* offs,
-                  const int* a_rows = nullptr) {
+                  const int* a_rows = nullptr, bool silu = false, float* pre_out = nullptr) {
     moe::GemmLaunch p{};
     p.a_rows = a_rows;
     p.a_div = k;
     p.a_total = T;
+    p.pre_out = pre_out;
     p.A = A;
     p.B = B;
     p.ab_dtype = MOE_BF16;
@@ -501,7 +502,7 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
     p.M_rows = M;
     p.N = N;
     p.K = K;
-    p.silu = false;
+    p.silu = silu;
     p.C = C;
     p.c_dtype = cdt;
     p.koff = kof;
@@ -519,17 +520,18 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
     step(moe::launch_fill_f32(static_cast<float*>(dw2), (long long)E * H * I * esize(grad_dtype) / 4, 0.0f, st));
     return launched(e, "backward");
   }
-  // forward intermediates, recomputed: gu = [g | u] (f32, token rows read through
-  // the permutation), h, y (f32)
+  // forward intermediates, recomputed: h (bf16) and its pre-activations gu = [g | u]
+  // (f32) from one SiLU*up GEMM reading token rows through the permutation; y (f32)
   step(moe::launch_pad_offsets(offsets, E, (int)R, koff, st));
-  step(gemm(x, w13, R, 2 * I, H, gu, MOE_F32, nullptr, 0, 0, E, offsets, sorted_rows));
-  step(moe::launch_silu_mul_rows(gu, offsets, E, (int)R, (int)I, ws + L.h, st));
+  step(gemm(x, w13, R, 2 * I, H, ws + L.h, MOE_BF16, nullptr, 0, 0, E, offsets, sorted_rows, true, gu));
   step(gemm(ws + L.h, w2, R, H, I, y, MOE_F32, nullptr, 0, 0, E, offsets));
   // routing-weight gradients and the scattered output gradient
   if (dtopk_weights)
     step(moe::launch_route_grad(dout, y, row_pos, offsets, E, (int)T, k, (int)H, dtopk_weights, st));
   step(moe::launch_expand_rows(dout, topk_weights, sorted_rows, offsets, E, (int)T, k, (int)H, ws + L.dy, st));
-  // data gradients: dh = dy W2 (on W2^T), SiLU*up backward, dx_perm = dgu W13 (on W13^T)
+  // data gradients: dh = dy W2 (on W2^T), SiLU*up backward, dx_perm = dgu W13 (on W13^T).
+  // (The SiLU*up backward stays a kernel of its own: in the dh GEMM's epilogue its gu
+  // loads stalled every tile, and the two together ran 118 us slower.)
   step(moe::launch_transpose_bf16(w2, E, (int)H, (int)I, ws + L.w2t, st));
   step(gemm(ws + L.dy, ws + L.w2t, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets));
   step(moe::launch_silu_bwd_rows(dh, gu, offsets, E, (int)R, (int)I, ws + L.dgu, st));

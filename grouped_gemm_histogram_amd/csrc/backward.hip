@@ -1,7 +1,8 @@
 // backward.hip -- the elementwise and data-movement steps of the layer's backward
-// (bf16 layers).  The GEMMs of the backward run on grouped_gemm_kernel: the two
-// data-gradient products on transposed weights, the two weight-gradient
-// products in its K-grouped mode.
+// (bf16 layers).  The GEMMs of the backward run on grouped_gemm_kernel: the
+// recomputed SiLU*up product (whose epilogue also keeps the f32 pre-activations
+// gu), the two data-gradient products on transposed weights, and the two
+// weight-gradient products in its K-grouped mode.
 //
 // The layer is the one of the LlamaFactory PR #10481 write-up (section 1):
 // h = SiLU(gate) * up per permuted row, y = W2 h, out[t] = sum_j w[t,j] y.  Its
@@ -11,7 +12,6 @@
 // a training NaN to exactly that).
 //
 //   expand:       dy[p]  = w[r] * dout[r / k]           (p < V; r = sorted_rows[p])
-//   silu_mul:     h[p]   = silu(g) * u                  from the fp32 pre-activation gu
 //   silu_bwd:     dgu[p] = [dh * u * silu'(g), dh * silu(g)]
 //   route_grad:   dw[r]  = dout[r / k] . y[row_pos[r]]  (0 for a sentinel slot)
 //   transposes:   weights [E, R, C] -> [E, C, R] (R, C multiples of 8); permuted
@@ -158,26 +158,6 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
   }
 }
 
-// h[p] = silu(g) * u for p < V, from gu = [g | u] fp32 [R, 2I]; 4 columns per thread.
-__global__ __launch_bounds__(256) void silu_mul_rows_kernel(const float* __restrict__ gu, const int* __restrict__ offsets,
-                                                            int E, int R, int I, uint16_t* __restrict__ h) {
-  const int V = clamp_off(offsets, E, R);
-  const long long n4 = (long long)V * (I / 4);
-  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (long long)gridDim.x * blockDim.x) {
-    const long long p = q / (I / 4);
-    const int c = (int)(q - p * (I / 4)) * 4;
-    const float4 g = *reinterpret_cast<const float4*>(gu + p * 2 * I + c);
-    const float4 u = *reinterpret_cast<const float4*>(gu + p * 2 * I + I + c);
-    *reinterpret_cast<uint2*>(h + p * I + c) =
-        make_uint2(pack_bf16x2(silu_mul(g.x, u.x), silu_mul(g.y, u.y)), pack_bf16x2(silu_mul(g.z, u.z), silu_mul(g.w, u.w)));
-  }
-}
-
-__device__ __forceinline__ float dsilu(float g) {
-  const float s = 1.0f / (1.0f + __expf(-g));
-  return s * (1.0f + g * (1.0f - s));
-}
-
 // dgu[p] = [dh * u * silu'(g), dh * silu(g)] for p < V; bf16 out.
 __global__ __launch_bounds__(256) void silu_bwd_rows_kernel(const float* __restrict__ dh, const float* __restrict__ gu,
                                                             const int* __restrict__ offsets, int E, int R, int I,
@@ -273,13 +253,6 @@ hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const i
     hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), R, C, offsets, koff, E, src_rows, src_div > 0 ? src_div : 1,
                        src_total, static_cast<uint16_t*>(dst), ldd);
-  return hipGetLastError();
-}
-
-hipError_t launch_silu_mul_rows(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream) {
-  if (R > 0)
-    hipLaunchKernelGGL(silu_mul_rows_kernel, grid1d((long long)R * (I / 4), 256 * 8), dim3(256), 0, stream, gu,
-                       offsets, E, R, I, static_cast<uint16_t*>(h));
   return hipGetLastError();
 }
 

@@ -43,4 +43,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// d silu(g) / dg = s (1 + g (1 - s)), s = sigmoid(g)
+__device__ __forceinline__ float dsilu(float g) {
+  const float s = 1.0f / (1.0f + __expf(-g));
+  return s * (1.0f + g * (1.0f - s));
+}
+
 }  // namespace moe

@@ -93,6 +93,10 @@ struct GemmArgs {
   const int* a_rows;
   int a_div;
   int a_total;
+  // SiLU*up with bf16 operands and C (M-grouped mode): when pre_out is set, also
+  // store the f32 pre-activations, gate at column c and up at column N_out + c of
+  // pre_out [M_rows, 2 N_out] (rows below offsets[E]; the layer's backward reads them).
+  float* pre_out;
 };
 
 #define MOE_INLINE __attribute__((always_inline))
@@ -991,6 +995,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           if (wn == 0 && g == 0) args.c_scales[(long long)(n0 / 128) * args.M_rows + m] = scale;
         }
       } else if constexpr (CT == CType::BF16) {
+        if constexpr (SILU) {
+          if (args.pre_out != nullptr && row_ok) {
+            float* pg = args.pre_out + m * 2 * N_out + cbase;
+#pragma unroll
+            for (int s = 0; s < SNO; ++s)
+              if (cbase + 4 * s + 4 <= N_out) {
+                *reinterpret_cast<float4*>(pg + 4 * s) = make_float4(acc[t][s][0], acc[t][s][1], acc[t][s][2], acc[t][s][3]);
+                *reinterpret_cast<float4*>(pg + N_out + 4 * s) =
+                    make_float4(acc[t][SNO + s][0], acc[t][SNO + s][1], acc[t][SNO + s][2], acc[t][SNO + s][3]);
+              }
+          }
+        }
         if (row_ok) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(args.C) + m * N_out + cbase;
           // 4*SNO contiguous columns, written as 8-column (16-byte) stores where
@@ -1150,6 +1166,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.lda = p.koff ? (int)p.lda : (int)p.K;
   a.ldb = p.koff ? (int)p.ldb : (int)p.K;
   if (p.koff && (p.ab_dtype != 1 || p.silu || p.c_dtype == 2)) return hipErrorInvalidValue;
+  a.pre_out = p.pre_out;
+  if (p.pre_out && (p.ab_dtype != 1 || !p.silu || p.c_dtype != 1 || p.koff)) return hipErrorInvalidValue;
   a.a_rows = p.a_rows;
   a.a_div = p.a_rows ? p.a_div : 1;
   a.a_total = p.a_rows ? (int)p.a_total : (int)p.M_rows;

@@ -46,6 +46,9 @@ struct GemmLaunch {
   const int* a_rows = nullptr;
   int a_div = 1;
   long long a_total = 0;
+  // bf16 operands and C, M-grouped mode: SiLU*up also stores the f32 pre-activations
+  // [M_rows, 2 N_out] (pre_out)
+  float* pre_out = nullptr;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,
@@ -60,7 +63,6 @@ hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void*
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
                                           const int* src_rows, int src_div, int src_total, void* dst, int ldd,
                                           hipStream_t stream);
-hipError_t launch_silu_mul_rows(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream);
 hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
                                 hipStream_t stream);
 hipError_t launch_expand_rows(const void* dout, const float* w, const int* sorted_rows, const int* offsets, int E,
