@@ -159,7 +159,8 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t 
  * valid row.  Rows [offsets[E], M_rows) of C are written as exact zeros
  * (their fp8 scales as 1.0) -- never left uninitialised ([T45621] section 3
  * traces a NaN to sentinel outputs that a kernel left unwritten).
- * Accumulation is fp32; C is rounded once (RNE).
+ * Accumulation is fp32; C is rounded once (RNE).  A must span under 4 GiB, and
+ * so must one expert's B (MOE_ERR_INVALID_ARG otherwise).
  */
 moe_status_t moe_grouped_gemm(const void* A, const float* a_scales, const void* B,
                               const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
