@@ -146,6 +146,10 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_DECODE_ROWS_PER_EXPERT
 #define MOE_DECODE_ROWS_PER_EXPERT 8
 #endif
+// m-tiles per block of an expert's tile order (see the tile decode)
+#ifndef MOE_M_BLOCK
+#define MOE_M_BLOCK 4
+#endif
 #ifndef MOE_DECODE_NARROW_ROWS_PER_EXPERT
 #define MOE_DECODE_NARROW_ROWS_PER_EXPERT 2
 #endif
@@ -393,8 +397,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       t.e = lo;
       const int mt_e = s_mt_pre[t.e + 1] - s_mt_pre[t.e];
       const int local = tile - s_mt_pre[t.e] * n_tiles;
-      nt = local / mt_e;
-      ml = local - nt * mt_e;
+      // the expert's m-tiles in blocks of up to MOE_M_BLOCK; within a block n-tile, then
+      // m-tile fastest, so that an XCD's consecutive tiles form a near-square block of
+      // activation and weight panels (an expert with few m-tiles is one block)
+      const int mb = min(local / (MOE_M_BLOCK * n_tiles), (mt_e - 1) / MOE_M_BLOCK);
+      const int h = min(MOE_M_BLOCK, mt_e - mb * MOE_M_BLOCK);
+      const int within = local - mb * MOE_M_BLOCK * n_tiles;
+      nt = within / h;
+      ml = mb * MOE_M_BLOCK + (within - nt * h);
       t.seg_end = off_at(t.e + 1);
       t.m0 = off_at(t.e) + ml * BM;
       t.out_row0 = t.m0;
