@@ -202,9 +202,38 @@ def warm(torch, call, at_least: int, seconds: float) -> int:
     return n
 
 
-def time_permute(g, torch, cfg, inp, aux, steps: int) -> dict:
+def time_events(torch, call, n: int, scrub=None) -> float:
+    """Mean device time (us) of call() over n calls, timed with HIP events on the stream the
+    library runs on.  Without scrub: one event pair around n back-to-back calls.  With scrub:
+    before every call (outside its event pair) the 512 MB buffer is read through once, so the
+    call's inputs are no longer in L2 or the 256 MB MALL and no dirty lines are left to flush."""
+    stream = torch.cuda.current_stream().cuda_stream
+    if scrub is None:
+        ev = HipEvents(2)
+        ev.record(0, stream)
+        for _ in range(n):
+            call()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        us = ev.ms(0, 1) / n * 1e3
+        ev.close()
+        return us
+    ev = HipEvents(2 * n)
+    for i in range(n):
+        scrub.sum()
+        ev.record(2 * i, stream)
+        call()
+        ev.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    us = sum(ev.ms(2 * i, 2 * i + 1) for i in range(n)) / n * 1e3
+    ev.close()
+    return us
+
+
+def time_permute(g, torch, cfg, inp, aux, steps: int, scrub) -> dict:
     """moe_permute on its own (the scatter step; the layer's gate/up GEMM reads token rows
-    through the permutation instead): V rows read and written, HIP events on its stream."""
+    through the permutation instead): V rows read and written.  `us` back to back (the token
+    rows stay in the MALL from call to call), `cold_us` with a 512 MB read between calls."""
     fp8 = cfg.dtype == "fp8"
     out_dt = torch.float8_e4m3fn if fp8 else inp.x.dtype
     xp = torch.empty(cfg.R, cfg.H, dtype=out_dt, device=inp.x.device)
@@ -213,20 +242,32 @@ def time_permute(g, torch, cfg, inp, aux, steps: int) -> dict:
     def call():
         g.permute(inp.x, aux.sorted_rows, aux.offsets, cfg.k, out_dtype=out_dt, out=xp, out_scales=xs)
     warm(torch, call, 5, 0.2)
-    ev = HipEvents(2)
-    stream = torch.cuda.current_stream().cuda_stream
     n = max(steps, 20)
-    ev.record(0, stream)
-    for _ in range(n):
-        call()
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    us = ev.ms(0, 1) / n * 1e3
-    ev.close()
+    us = time_events(torch, call, n)
+    cold = time_events(torch, call, n, scrub)
     esz = inp.x.element_size()
     V = cfg.V
     moved = V * cfg.H * esz + (V * cfg.H + V * (cfg.H // 128) * 4 if fp8 else V * cfg.H * esz)
-    return {"us": us, "bytes": moved, "gbs": moved / (us * 1e-6) / 1e9}
+    return {"us": us, "bytes": moved, "gbs": moved / (us * 1e-6) / 1e9,
+            "cold_us": cold, "cold_gbs": moved / (cold * 1e-6) / 1e9}
+
+
+def time_combine(g, torch, cfg, inp, aux, steps: int, scrub) -> dict:
+    """moe_unpermute_combine on its own over bf16 rows y [R, H] (values from the seeded hidden
+    states; only the access pattern matters): V rows + T output rows + 8 B per slot, back to
+    back and with a 512 MB read between calls."""
+    y = inp.x.repeat_interleave(cfg.k, dim=0)[: cfg.R].to(torch.bfloat16).contiguous()
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=inp.x.device)
+
+    def call():
+        g.unpermute_combine(y, aux.row_pos, aux.topk_weights, aux.offsets, cfg.k, out=out)
+    warm(torch, call, 5, 0.2)
+    n = max(steps, 20)
+    us = time_events(torch, call, n)
+    cold = time_events(torch, call, n, scrub)
+    moved = cfg.V * cfg.H * 2 + cfg.T * cfg.H * 2 + 8 * cfg.T * cfg.k
+    return {"us": us, "bytes": moved, "gbs": moved / (us * 1e-6) / 1e9,
+            "cold_us": cold, "cold_gbs": moved / (cold * 1e-6) / 1e9}
 
 
 def time_decode(g, torch, cfg, inp, steps: int, tokens=(1, 8, 64)) -> list:
@@ -382,7 +423,10 @@ def main() -> int:
     device_ms = sum(ev.ms(i * (nst + 1), i * (nst + 1) + nst) for i in range(args.steps)) / args.steps
     ev.close()
 
-    permute = time_permute(g, torch, cfg, inp, aux, args.steps)
+    scrub = torch.ones(64 << 20, dtype=torch.int64, device=dev)   # 512 MB, read to evict caches
+    permute = time_permute(g, torch, cfg, inp, aux, args.steps, scrub)
+    combine = time_combine(g, torch, cfg, inp, aux, args.steps, scrub)
+    del scrub
 
     decode = None
     if cfg.dtype == "bf16" and not args.no_decode:
@@ -453,6 +497,7 @@ def main() -> int:
         "device_ms_per_step": device_ms,
         "combine_gbs": combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9,
         "permute_standalone": permute,
+        "combine_standalone": combine,
         "valid_rows_offsets_last": offsets_host[-1],
         "predicted_mfma_flops": {"gemm_gate_up": pred_gu, "gemm_down": pred_dn},
         "roofline": roofline,
