@@ -409,7 +409,7 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
 namespace {
 
 struct BwdLayout {
-  size_t koff, gu, h, y, dy, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
+  size_t koff, gu, h, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
   long long ldd;   // row stride of the expert-padded transposes (elements)
 };
 
@@ -426,8 +426,6 @@ BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
   L.koff = take((size_t)(E + 1) * 4);
   L.gu = take((size_t)R * 2 * I * 4);
   L.h = take((size_t)R * I * 2);
-  L.y = take((size_t)R * H * 4);
-  L.dy = take((size_t)R * H * 2);
   L.dh = take((size_t)R * I * 4);
   L.dgu = take((size_t)R * 2 * I * 2);
   L.dxp = take((size_t)R * H * 4);
@@ -481,7 +479,6 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
   hipStream_t st = as_stream(stream);
   int* koff = reinterpret_cast<int*>(ws + L.koff);
   float* gu = reinterpret_cast<float*>(ws + L.gu);
-  float* y = reinterpret_cast<float*>(ws + L.y);
   float* dh = reinterpret_cast<float*>(ws + L.dh);
   float* dxp = reinterpret_cast<float*>(ws + L.dxp);
   float* ones = reinterpret_cast<float*>(ws + L.ones);
@@ -521,20 +518,18 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
     return launched(e, "backward");
   }
   // forward intermediates, recomputed: h (bf16) and its pre-activations gu = [g | u]
-  // (f32) from one SiLU*up GEMM reading token rows through the permutation; y (f32)
+  // (f32) from one SiLU*up GEMM reading token rows through the permutation
   step(moe::launch_pad_offsets(offsets, E, (int)R, koff, st));
   step(gemm(x, w13, R, 2 * I, H, ws + L.h, MOE_BF16, nullptr, 0, 0, E, offsets, sorted_rows, true, gu));
-  step(gemm(ws + L.h, w2, R, H, I, y, MOE_F32, nullptr, 0, 0, E, offsets));
-  // routing-weight gradients and the scattered output gradient
-  if (dtopk_weights)
-    step(moe::launch_route_grad(dout, y, row_pos, offsets, E, (int)T, k, (int)H, dtopk_weights, st));
-  step(moe::launch_expand_rows(dout, topk_weights, sorted_rows, offsets, E, (int)T, k, (int)H, ws + L.dy, st));
-  // data gradients: dh = dy W2 (on W2^T), SiLU*up backward, dx_perm = dgu W13 (on W13^T).
-  // (The SiLU*up backward stays a kernel of its own: in the dh GEMM's epilogue its gu
-  // loads stalled every tile, and the two together ran 118 us slower.)
+  // data gradients: dh1 = dout W2 per routed row (on W2^T, dout rows read through the
+  // permutation, routing weight not yet applied); then per slot the routing-weight
+  // gradient dw = dh1 . h (= dout . y, so y is never recomputed) and the SiLU*up
+  // backward of dh = w dh1; dx_perm = dgu W13 (on W13^T).  (The SiLU*up backward stays
+  // a kernel of its own: in the GEMM's epilogue its gu loads stalled every tile.)
   step(moe::launch_transpose_bf16(w2, E, (int)H, (int)I, ws + L.w2t, st));
-  step(gemm(ws + L.dy, ws + L.w2t, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets));
-  step(moe::launch_silu_bwd_rows(dh, gu, offsets, E, (int)R, (int)I, ws + L.dgu, st));
+  step(gemm(dout, ws + L.w2t, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets, sorted_rows));
+  step(moe::launch_silu_bwd_route(dh, gu, ws + L.h, topk_weights, row_pos, offsets, E, (int)R, (int)I, ws + L.dgu,
+                                  dtopk_weights, st));
   step(moe::launch_transpose_bf16(w13, E, (int)(2 * I), (int)H, ws + L.w13t, st));
   step(gemm(ws + L.dgu, ws + L.w13t, R, H, 2 * I, dxp, MOE_F32, nullptr, 0, 0, E, offsets));
   step(moe::launch_fill_f32(ones, R, 1.0f, st));
@@ -542,16 +537,17 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
                            grad_dtype == MOE_BF16, st));
   // weight gradients: K-grouped GEMMs over each expert's rows, on expert-padded transposes
   const int ldd = (int)L.ldd;
-  step(moe::launch_transpose_segments_bf16(ws + L.dy, (int)R, (int)H, offsets, koff, E, nullptr, 1, (int)R, ws + L.ta,
-                                           ldd, st));
-  step(moe::launch_transpose_segments_bf16(ws + L.h, (int)R, (int)I, offsets, koff, E, nullptr, 1, (int)R, ws + L.tb,
-                                           ldd, st));
+  // dy = w dout per routed row, formed while transposing (dout rows through the permutation)
+  step(moe::launch_transpose_segments_bf16(dout, (int)R, (int)H, offsets, koff, E, sorted_rows, k, (int)T,
+                                           topk_weights, ws + L.ta, ldd, st));
+  step(moe::launch_transpose_segments_bf16(ws + L.h, (int)R, (int)I, offsets, koff, E, nullptr, 1, (int)R, nullptr,
+                                           ws + L.tb, ldd, st));
   step(gemm(ws + L.ta, ws + L.tb, H, I, ldd, dw2, gdt, koff, ldd, ldd, E, nullptr));
   step(moe::launch_transpose_segments_bf16(ws + L.dgu, (int)R, (int)(2 * I), offsets, koff, E, nullptr, 1, (int)R,
-                                           ws + L.ta, ldd, st));
+                                           nullptr, ws + L.ta, ldd, st));
   // x's rows of each expert, read through the permutation
-  step(moe::launch_transpose_segments_bf16(x, (int)R, (int)H, offsets, koff, E, sorted_rows, k, (int)T, ws + L.tb,
-                                           ldd, st));
+  step(moe::launch_transpose_segments_bf16(x, (int)R, (int)H, offsets, koff, E, sorted_rows, k, (int)T, nullptr,
+                                           ws + L.tb, ldd, st));
   step(gemm(ws + L.ta, ws + L.tb, 2 * I, H, ldd, dw13, gdt, koff, ldd, ldd, E, nullptr));
   return launched(e, "backward");
 }

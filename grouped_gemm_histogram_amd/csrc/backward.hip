@@ -11,9 +11,12 @@
 // own is left unwritten (the transformers PR #45621 write-up, section 3, traces
 // a training NaN to exactly that).
 //
-//   expand:       dy[p]  = w[r] * dout[r / k]           (p < V; r = sorted_rows[p])
-//   silu_bwd:     dgu[p] = [dh * u * silu'(g), dh * silu(g)]
-//   route_grad:   dw[r]  = dout[r / k] . y[row_pos[r]]  (0 for a sentinel slot)
+//   data gradient: dh1[p] = dout[r / k] W2_e           (p < V; r = sorted_rows[p]; the
+//                  unweighted product, a GEMM reading dout rows through the permutation)
+//   silu_bwd:     dw[r]  = dh1[p] . h[p]                (0 for a sentinel slot), since
+//                  dL/dw[r] = dout[r/k] . y[p] = dout[r/k] . (W2_e h[p]) = (dout[r/k] W2_e) . h[p];
+//                  dh = w[r] dh1[p];  dgu[p] = [dh * u * silu'(g), dh * silu(g)]
+//   weighted rows: dy[p] = w[r] * dout[r / k], formed while transposing for dW2
 //   transposes:   weights [E, R, C] -> [E, C, R] (R, C multiples of 8); permuted
 //                 activations [R, C] -> expert-major blocks [C, round_up(M_e, 64)]
 //                 (rows of an expert contiguous, padding columns zero), so that every
@@ -32,8 +35,6 @@ constexpr int kMaxE = 1024;
 __device__ __forceinline__ int clamp_off(const int* offsets, int e, int R) {
   return min(max(offsets[e], 0), R);
 }
-
-__device__ __forceinline__ float bf16_at(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 
 }  // namespace
 
@@ -114,13 +115,15 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 // [0, koff[E]); a block lies inside one expert's range since every koff[e] is a
 // multiple of 64.  C a multiple of 8; koff[E] <= ldd bounds the grid.  With
 // src_rows set, row p is read from row src_rows[p] / src_div of src (token rows
-// through the permutation; src has src_total rows, indices clamped into them).
+// through the permutation; src has src_total rows, indices clamped into them),
+// and with src_scale also set it is multiplied by src_scale[src_rows[p]] (one
+// rounding to bf16 of the fp32 product).
 __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint16_t* __restrict__ src, int R,
                                                                       int C, const int* __restrict__ offsets,
                                                                       const int* __restrict__ koff, int E,
                                                                       const int* __restrict__ src_rows, int src_div,
-                                                                      int src_total, uint16_t* __restrict__ dst,
-                                                                      int ldd) {
+                                                                      int src_total, const float* __restrict__ src_scale,
+                                                                      uint16_t* __restrict__ dst, int ldd) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int Vp = min(koff[E], ldd);
@@ -144,8 +147,21 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
     const int p = p0 + r;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (p < pend && c0 + 8 * q < C) {
-      const int sr = src_rows != nullptr ? min(max(src_rows[p] / src_div, 0), src_total - 1) : p;
-      v = *reinterpret_cast<const uint4*>(src + (size_t)sr * C + c0 + 8 * q);
+      if (src_rows != nullptr) {
+        const int fr = min(max(src_rows[p], 0), src_total * src_div - 1);
+        v = *reinterpret_cast<const uint4*>(src + (size_t)(fr / src_div) * C + c0 + 8 * q);
+        if (src_scale != nullptr) {
+          const float sc = src_scale[fr];
+          const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = pack_bf16x2(sc * bf16_bits_to_f32(in[i] & 0xffffu), sc * bf16_bits_to_f32(in[i] >> 16));
+          v = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      } else {
+        v = *reinterpret_cast<const uint4*>(src + (size_t)p * C + c0 + 8 * q);
+      }
     }
     *reinterpret_cast<uint4*>(tile + tp_pos(r, q)) = v;
   }
@@ -158,55 +174,15 @@ __global__ __launch_bounds__(256) void transpose_segments_bf16_kernel(const uint
   }
 }
 
-// dgu[p] = [dh * u * silu'(g), dh * silu(g)] for p < V; bf16 out.
-__global__ __launch_bounds__(256) void silu_bwd_rows_kernel(const float* __restrict__ dh, const float* __restrict__ gu,
-                                                            const int* __restrict__ offsets, int E, int R, int I,
-                                                            uint16_t* __restrict__ dgu) {
-  const int V = clamp_off(offsets, E, R);
-  const long long n4 = (long long)V * (I / 4);
-  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += (long long)gridDim.x * blockDim.x) {
-    const long long p = q / (I / 4);
-    const int c = (int)(q - p * (I / 4)) * 4;
-    const float4 d = *reinterpret_cast<const float4*>(dh + p * I + c);
-    const float4 g = *reinterpret_cast<const float4*>(gu + p * 2 * I + c);
-    const float4 u = *reinterpret_cast<const float4*>(gu + p * 2 * I + I + c);
-    const float dg[4] = {d.x * u.x * dsilu(g.x), d.y * u.y * dsilu(g.y), d.z * u.z * dsilu(g.z), d.w * u.w * dsilu(g.w)};
-    const float du[4] = {d.x * silu_mul(g.x, 1.0f), d.y * silu_mul(g.y, 1.0f), d.z * silu_mul(g.z, 1.0f),
-                         d.w * silu_mul(g.w, 1.0f)};
-    *reinterpret_cast<uint2*>(dgu + p * 2 * I + c) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-    *reinterpret_cast<uint2*>(dgu + p * 2 * I + I + c) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-  }
-}
-
-// dy[p] = w[r] * dout[r / k] (bf16) for p < V; one wave per row, 8 columns per lane step.
-__global__ __launch_bounds__(256) void expand_rows_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ w,
-                                                          const int* __restrict__ sorted_rows, const int* __restrict__ offsets,
-                                                          int E, int T, int k, int H, uint16_t* __restrict__ dy) {
-  const int R = T * k;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (p >= clamp_off(offsets, E, R)) return;
-  const int r = sorted_rows[p];
-  if (r < 0 || r >= R) return;   // inconsistent permutation: leave the row unwritten
-  const float wr = w[r];
-  const uint4* s = reinterpret_cast<const uint4*>(dout + (size_t)(r / k) * H);
-  uint4* d = reinterpret_cast<uint4*>(dy + (size_t)p * H);
-  for (int c = lane; c < H / 8; c += kWave) {
-    const uint4 v = s[c];
-    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = pack_bf16x2(wr * bf16_bits_to_f32(in[i] & 0xffffu), wr * bf16_bits_to_f32(in[i] >> 16));
-    d[c] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
-// dw[r] = dout[r / k] . y[row_pos[r]] over valid slots, 0 otherwise; one wave per slot.
-__global__ __launch_bounds__(256) void route_grad_kernel(const uint16_t* __restrict__ dout, const float* __restrict__ y,
-                                                         const int* __restrict__ row_pos, const int* __restrict__ offsets,
-                                                         int E, int T, int k, int H, float* __restrict__ dw) {
-  const int R = T * k;
+// One wave per slot r, with p = row_pos[r] (valid when p < V):
+//   dw[r]  = dh1[p] . h[p]   (fp32, lanes then a butterfly; 0 for a sentinel slot)
+//   dgu[p] = [dh * u * silu'(g), dh * silu(g)] with dh = w[r] * dh1[p] (bf16 out)
+// dw may be null (no routing-weight gradient wanted).
+__global__ __launch_bounds__(256) void silu_bwd_route_kernel(const float* __restrict__ dh1, const float* __restrict__ gu,
+                                                             const uint16_t* __restrict__ h, const float* __restrict__ w,
+                                                             const int* __restrict__ row_pos,
+                                                             const int* __restrict__ offsets, int E, int R, int I,
+                                                             uint16_t* __restrict__ dgu, float* __restrict__ dw) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (r >= R) return;
@@ -214,12 +190,37 @@ __global__ __launch_bounds__(256) void route_grad_kernel(const uint16_t* __restr
   const int p = row_pos[r];
   float acc = 0.0f;
   if (p >= 0 && p < V) {
-    const uint16_t* dt = dout + (size_t)(r / k) * H;
-    const float* yp = y + (size_t)p * H;
-    for (int c = lane; c < H; c += kWave) acc = fmaf(bf16_at(dt + c), yp[c], acc);
+    const float wr = w[r];
+    const float* d = dh1 + (size_t)p * I;
+    const float* g = gu + (size_t)p * 2 * I;
+    const float* u = g + I;
+    const uint16_t* hp = h + (size_t)p * I;
+    uint16_t* og = dgu + (size_t)p * 2 * I;
+    uint16_t* ou = og + I;
+    for (int c = lane * 4; c < I; c += kWave * 4) {
+      const float4 d4 = *reinterpret_cast<const float4*>(d + c);
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c);
+      const float4 u4 = *reinterpret_cast<const float4*>(u + c);
+      const uint2 h4 = *reinterpret_cast<const uint2*>(hp + c);
+      acc = fmaf(d4.x, bf16_bits_to_f32(h4.x & 0xffffu), acc);
+      acc = fmaf(d4.y, bf16_bits_to_f32(h4.x >> 16), acc);
+      acc = fmaf(d4.z, bf16_bits_to_f32(h4.y & 0xffffu), acc);
+      acc = fmaf(d4.w, bf16_bits_to_f32(h4.y >> 16), acc);
+      const float dd[4] = {wr * d4.x, wr * d4.y, wr * d4.z, wr * d4.w};
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+      const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+      float dg[4], du[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dg[i] = dd[i] * uu[i] * dsilu(gg[i]);
+        du[i] = dd[i] * silu_mul(gg[i], 1.0f);
+      }
+      *reinterpret_cast<uint2*>(og + c) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+      *reinterpret_cast<uint2*>(ou + c) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+    }
     acc = wave_sum(acc);
   }
-  if (lane == 0) dw[r] = acc;
+  if (dw != nullptr && lane == 0) dw[r] = acc;
 }
 
 __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ p, long long n, float v) {
@@ -247,39 +248,21 @@ hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void*
 }
 
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
-                                          const int* src_rows, int src_div, int src_total, void* dst, int ldd,
-                                          hipStream_t stream) {
+                                          const int* src_rows, int src_div, int src_total, const float* src_scale,
+                                          void* dst, int ldd, hipStream_t stream) {
   if (R > 0 && C > 0)
     hipLaunchKernelGGL(transpose_segments_bf16_kernel, dim3((ldd + 63) / 64, (C + 63) / 64), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(src), R, C, offsets, koff, E, src_rows, src_div > 0 ? src_div : 1,
-                       src_total, static_cast<uint16_t*>(dst), ldd);
+                       src_total, src_scale, static_cast<uint16_t*>(dst), ldd);
   return hipGetLastError();
 }
 
-hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
-                                hipStream_t stream) {
+hipError_t launch_silu_bwd_route(const float* dh1, const float* gu, const void* h, const float* w,
+                                 const int* row_pos, const int* offsets, int E, int R, int I, void* dgu, float* dw,
+                                 hipStream_t stream) {
   if (R > 0)
-    hipLaunchKernelGGL(silu_bwd_rows_kernel, grid1d((long long)R * (I / 4), 256 * 8), dim3(256), 0, stream, dh, gu,
-                       offsets, E, R, I, static_cast<uint16_t*>(dgu));
-  return hipGetLastError();
-}
-
-hipError_t launch_expand_rows(const void* dout, const float* w, const int* sorted_rows, const int* offsets, int E,
-                              int T, int k, int H, void* dy, hipStream_t stream) {
-  const long long R = (long long)T * k;
-  if (R > 0)
-    hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(dout), w, sorted_rows, offsets, E, T, k, H,
-                       static_cast<uint16_t*>(dy));
-  return hipGetLastError();
-}
-
-hipError_t launch_route_grad(const void* dout, const float* y, const int* row_pos, const int* offsets, int E, int T,
-                             int k, int H, float* dw, hipStream_t stream) {
-  const long long R = (long long)T * k;
-  if (R > 0)
-    hipLaunchKernelGGL(route_grad_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(dout), y, row_pos, offsets, E, T, k, H, dw);
+    hipLaunchKernelGGL(silu_bwd_route_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, dh1, gu,
+                       static_cast<const uint16_t*>(h), w, row_pos, offsets, E, R, I, static_cast<uint16_t*>(dgu), dw);
   return hipGetLastError();
 }
 

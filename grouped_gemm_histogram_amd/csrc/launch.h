@@ -59,16 +59,15 @@ bool use_decode_tiles(long long M_rows, int E);
 // backward steps (backward.hip)
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);
 hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream);
-// src_rows nullable: row p of the segments is src row src_rows[p] / src_div (of src_total)
+// src_rows nullable: row p of the segments is src row src_rows[p] / src_div (of src_total),
+// times src_scale[src_rows[p]] when src_scale is set
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,
-                                          const int* src_rows, int src_div, int src_total, void* dst, int ldd,
-                                          hipStream_t stream);
-hipError_t launch_silu_bwd_rows(const float* dh, const float* gu, const int* offsets, int E, int R, int I, void* dgu,
-                                hipStream_t stream);
-hipError_t launch_expand_rows(const void* dout, const float* w, const int* sorted_rows, const int* offsets, int E,
-                              int T, int k, int H, void* dy, hipStream_t stream);
-hipError_t launch_route_grad(const void* dout, const float* y, const int* row_pos, const int* offsets, int E, int T,
-                             int k, int H, float* dw, hipStream_t stream);
+                                          const int* src_rows, int src_div, int src_total, const float* src_scale,
+                                          void* dst, int ldd, hipStream_t stream);
+// per slot r (p = row_pos[r] < V): dw[r] = dh1[p] . h[p]; dgu[p] = SiLU*up backward of w[r] * dh1[p]
+hipError_t launch_silu_bwd_route(const float* dh1, const float* gu, const void* h, const float* w,
+                                 const int* row_pos, const int* offsets, int E, int R, int I, void* dgu, float* dw,
+                                 hipStream_t stream);
 hipError_t launch_fill_f32(float* p, long long n, float v, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const float* weights,

@@ -314,8 +314,10 @@ size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_
  *   dW2[e] = sum over the expert's rows of dy_p h_p^T
  *   dW13[e] = sum over the expert's rows of dgu_p x_t^T
  *
- * The forward pre-activations are recomputed here (the same grouped GEMMs as
- * moe_forward, kept in f32); nothing of the forward's workspace is needed.
+ * The forward's h and pre-activations [g | u] are recomputed here (its SiLU*up
+ * grouped GEMM, pre-activations kept in f32); nothing of the forward's workspace
+ * is needed.  y_p is not: dw[r] is evaluated as (W2[e]^T dout[t]) . h_p, the same
+ * quantity, from the unweighted product W2[e]^T dout[t] that dh_p = w[r] times.
  *
  *   x, w13, w2, dout  MOE_BF16 (dtype must be MOE_BF16): x, dout [T, H];
  *                w13 [E, 2I, H], w2 [E, H, I].  H and I multiples of 8.
@@ -327,7 +329,8 @@ size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_
  *                experts with no rows get exact zeros).
  *   dtopk_weights f32 [T, k]: dw; 0 for sentinel slots.  Nullable.
  *   workspace    >= moe_backward_workspace(T, H, I, E, k) bytes.
- * Accumulation is fp32; the MFMA operands dy, h, dgu and x are bf16.
+ * Accumulation is fp32.  MFMA operands are bf16: dout (the routing weight is
+ * applied to the fp32 product), dy rounded once (for dW2), h, dgu and x.
  */
 moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dtype_t dtype,
                           int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
