@@ -54,7 +54,8 @@ def test_route_topk(T, E, k, ties):
 
 # R <= 1024 runs the single-workgroup kernel, larger R the three-kernel chunked path
 OFFSET_CASES = [(1, 1), (100, 3), (1000, 8), (1024, 32), (1024, 1024), (64, 1024), (700, 256),
-                (1025, 8), (4096, 129), (16384, 128), (65536, 256), (70000, 1024), (5000, 1024), (3000, 1)]
+                (1025, 8), (4096, 129), (16384, 128), (16384, 32), (65536, 256), (65536, 1), (17000, 1024),
+                (70000, 1024), (70000, 8), (40000, 1024), (5000, 1024), (3000, 1)]
 
 
 @pytest.mark.parametrize("R,E", OFFSET_CASES)
