@@ -215,6 +215,10 @@ GEMM_CASES = [
     ("bf16", 900, 850, 5, 2 * 1408, 384, "silu_mul"),
     ("bf16", 700, 700, 3, 1412 - 4, 256, "none"),
     ("bf16", 500, 480, 4, 2 * 104, 192, "silu_mul"),
+    # no epilogue, N = 2880 (15 weight tiles of 192); up to 1024 experts in one launch
+    ("bf16", 1300, 1250, 4, 2880, 192, "none"),
+    ("bf16", 9000, 8900, 1022, 200, 64, "none"),
+    ("bf16", 9000, 8900, 1024, 200, 64, "none"),
     ("f32", 500, 420, 5, 2 * 100, 96, "silu_mul"),
     ("f32", 500, 500, 5, 132, 68, "none"),
     # decode-size launches (at most 8 rows per expert): 16-row tiles, ragged N and K tails
