@@ -8,7 +8,8 @@
 // stops before it, and the permutation places bin E last.
 //
 // Three small launches, no atomics on global memory, deterministic:
-//   1. hist:    one workgroup per chunk of rows, LDS histogram over E+1 bins.
+//   1. hist:    one workgroup per chunk of rows (256 rows up to 16384 rows, else
+//               1024), LDS histogram over E+1 bins.
 //   2. scan:    one workgroup; per-bin exclusive scan over chunks, then the
 //               exclusive scan over bins -> offsets and each chunk's base.
 //   3. scatter: one wave per chunk walks its rows in order, 64 at a time; a
@@ -22,19 +23,27 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;      // rows per chunk
+constexpr int kChunk = 1024;      // rows per chunk of large launches (and the one-workgroup limit)
+constexpr int kSmallChunk = 256;  // rows per chunk up to kSmallChunkMaxRows rows
+constexpr long long kSmallChunkMaxRows = 16384;
+
+// Rows per chunk for R rows: short chunks shorten each scatter wave's serial walk;
+// beyond kSmallChunkMaxRows rows the longer chunks keep the per-bin scan over chunks short.
+__host__ __device__ inline int chunk_rows(long long R) {
+  return R <= kSmallChunkMaxRows ? kSmallChunk : kChunk;
+}
 constexpr int kMaxBins = 1025;    // E + 1 with E <= 1024
 
 __device__ __forceinline__ int bin_of(int id, int E) { return (id >= 0 && id < E) ? id : E; }
 
-__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, int R, int E,
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, int R, int E, int chunk,
                                                    int* __restrict__ chunk_hist) {
   __shared__ int h[kMaxBins];
   const int nb = E + 1;
   for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0;
   __syncthreads();
-  const int r0 = blockIdx.x * kChunk;
-  const int r1 = min(R, r0 + kChunk);
+  const int r0 = blockIdx.x * chunk;
+  const int r1 = min(R, r0 + chunk);
   for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) atomicAdd(&h[bin_of(ids[r], E)], 1);
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += blockDim.x) chunk_hist[(size_t)blockIdx.x * nb + i] = h[i];
@@ -86,15 +95,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist
   }
 }
 
-// One wave places rows [r0, r1) (at most one chunk) in order; cursor[b] (LDS) holds the
-// next position of bin b and is advanced.
+// One wave places rows [r0, r1) (at most kSteps * 64 rows) in order; cursor[b] (LDS)
+// holds the next position of bin b and is advanced.
+template <int kSteps>
 __device__ __forceinline__ void scatter_rows(const int* __restrict__ ids, int r0, int r1, int E, int id_bits,
                                              int* cursor, int* __restrict__ sorted_rows,
                                              int* __restrict__ row_pos) {
   const int lane = lane_id();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   // all of the chunk's ids are loaded up front (one round trip instead of one per step)
-  constexpr int kSteps = kChunk / kWave;
   int keys[kSteps];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
@@ -128,7 +137,8 @@ __device__ __forceinline__ void scatter_rows(const int* __restrict__ ids, int r0
   }
 }
 
-// One wave per chunk.
+// One wave per chunk of kSteps * 64 rows.
+template <int kSteps>
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int R, int E,
                                                      int id_bits,
                                                      const int* __restrict__ chunk_base,
@@ -138,8 +148,9 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   const int nb = E + 1;
   for (int i = lane_id(); i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i];
   __syncthreads();
-  const int r0 = blockIdx.x * kChunk;
-  scatter_rows(ids, r0, min(R, r0 + kChunk), E, id_bits, cursor, sorted_rows, row_pos);
+  constexpr int chunk = kSteps * kWave;
+  const int r0 = blockIdx.x * chunk;
+  scatter_rows<kSteps>(ids, r0, min(R, r0 + chunk), E, id_bits, cursor, sorted_rows, row_pos);
 }
 
 // R <= kChunk: histogram, bin scan and scatter in one workgroup of 1024 threads.
@@ -168,32 +179,38 @@ __global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restr
     tot[src ^ 1][b] = base;
   }
   __syncthreads();
-  if (threadIdx.x < kWave) scatter_rows(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
+  if (threadIdx.x < kWave) scatter_rows<kChunk / kWave>(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
 }
 
 size_t build_offsets_workspace_bytes(long long R, int E) {
-  const long long nchunks = (R + kChunk - 1) / kChunk;
+  const long long nchunks = (R + chunk_rows(R) - 1) / chunk_rows(R);
   return (size_t)(nchunks > 0 ? nchunks : 1) * (size_t)(E + 1) * sizeof(int);
 }
 
 hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int* sorted_rows,
                                 int* row_pos, void* workspace, hipStream_t stream) {
-  const int nchunks = (R + kChunk - 1) / kChunk;
+  const int chunk = chunk_rows(R);
+  const int nchunks = (R + chunk - 1) / chunk;
   int* chunk_hist = static_cast<int*>(workspace);
   int id_bits = 1;
   while ((1 << id_bits) <= E) ++id_bits;   // bins 0..E need id_bits bits
-  if (nchunks <= 1) {
+  if (R <= kChunk) {
     hipLaunchKernelGGL(offsets_single_kernel, dim3(1), dim3(1024), 0, stream, ids, R, E, id_bits, offsets,
                        sorted_rows, row_pos);
     return hipGetLastError();
   }
   if (nchunks > 0)
-    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, chunk_hist);
+    hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, chunk, chunk_hist);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E,
                      offsets);
-  if (nchunks > 0)
-    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), 0, stream, ids, R, E, id_bits,
-                       chunk_hist, sorted_rows, row_pos);
+  if (nchunks > 0) {
+    if (chunk == kSmallChunk)
+      hipLaunchKernelGGL(scatter_kernel<kSmallChunk / kWave>, dim3(nchunks), dim3(64), 0, stream, ids, R, E,
+                         id_bits, chunk_hist, sorted_rows, row_pos);
+    else
+      hipLaunchKernelGGL(scatter_kernel<kChunk / kWave>, dim3(nchunks), dim3(64), 0, stream, ids, R, E, id_bits,
+                         chunk_hist, sorted_rows, row_pos);
+  }
   return hipGetLastError();
 }
 

@@ -52,10 +52,12 @@ def test_route_topk(T, E, k, ties):
 
 # ------------------------------------------------------------------------------------ offsets
 
-# R <= 1024 runs the single-workgroup kernel, larger R the three-kernel chunked path
+# R <= 1024 runs the single-workgroup kernel; larger R the three-kernel chunked path, in
+# chunks of 256 rows up to 16384 rows and of 1024 rows beyond
 OFFSET_CASES = [(1, 1), (100, 3), (1000, 8), (1024, 32), (1024, 1024), (64, 1024), (700, 256),
-                (1025, 8), (4096, 129), (16384, 128), (16384, 32), (65536, 256), (65536, 1), (17000, 1024),
-                (70000, 1024), (70000, 8), (40000, 1024), (5000, 1024), (3000, 1)]
+                (1025, 8), (1300, 5), (4096, 129), (16384, 128), (16384, 32), (16384, 1024), (16385, 8),
+                (65536, 256), (65536, 1), (17000, 1024), (70000, 1024), (70000, 8), (40000, 1024),
+                (5000, 1024), (3000, 1)]
 
 
 @pytest.mark.parametrize("R,E", OFFSET_CASES)
