@@ -10,8 +10,10 @@
 // Three small launches, no atomics on global memory, deterministic:
 //   1. hist:    one workgroup per chunk of rows (256 rows up to 16384 rows, else
 //               1024), LDS histogram over E+1 bins.
-//   2. scan:    one workgroup; per-bin exclusive scan over chunks, then the
-//               exclusive scan over bins -> offsets and each chunk's base.
+//   2. scan:    one workgroup; per-bin exclusive scan over chunks (a wave per
+//               bin, lanes over chunks), then the exclusive scan over bins ->
+//               offsets; a chunk's cursor for a bin is its place in the bin plus
+//               the bin's offset.
 //   3. scatter: one wave per chunk walks its rows in order, 64 at a time; a
 //               row's rank among equal ids in the same 64 comes from ballots
 //               over the id bits (lanes with equal ids), so ties keep flat
@@ -49,28 +51,33 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, 
   for (int i = threadIdx.x; i < nb; i += blockDim.x) chunk_hist[(size_t)blockIdx.x * nb + i] = h[i];
 }
 
-// One workgroup of 1024 threads.  chunk_hist [nchunks][E+1] becomes, in place,
-// the first permuted position of each (chunk, bin).
+// One workgroup of 1024 threads.  chunk_hist [nchunks][E+1] becomes, in place, each
+// (chunk, bin)'s first position within its bin (the exclusive scan of the bin's counts
+// over chunks); offsets[b] is the bin's base (the exclusive scan of the bin totals), which
+// the scatter adds.  A wave scans one bin at a time, 64 chunks per step (lanes over
+// chunks, carried from step to step), so the loads of a bin's counts go out together.
 __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist, int nchunks,
                                                     int E, int* __restrict__ offsets) {
   __shared__ int tot[2][kMaxBins + 1];
   const int nb = E + 1;
-  // per bin, exclusive scan over chunks; counts are loaded kBatch at a time so
-  // the loads of a batch are in flight together
-  constexpr int kBatch = 16;
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    int run = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-      int v[kBatch];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  constexpr int kWaves = 1024 / kWave;
+  for (int b = wave; b < nb; b += kWaves) {
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+      const int c = c0 + lane;
+      const int v = (c < nchunks) ? chunk_hist[(size_t)c * nb + b] : 0;
+      int x = v;   // inclusive scan over the lanes
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * nb + b] : 0;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * nb + b] = run;
-        run += v[i];
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
       }
+      if (c < nchunks) chunk_hist[(size_t)c * nb + b] = carry + x - v;
+      carry += __shfl(x, kWave - 1, kWave);
     }
-    tot[0][b] = run;
+    if (lane == 0) tot[0][b] = carry;
   }
   __syncthreads();
   // Hillis-Steele inclusive scan over the nb bin totals.
@@ -81,18 +88,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist
     __syncthreads();
     src ^= 1;
   }
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const int base = (b == 0) ? 0 : tot[src][b - 1];   // exclusive
-    offsets[b] = base;                                  // offsets[E] = valid rows
-    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-      int v[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * nb + b] : 0;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * nb + b] = v[i] + base;
-    }
-  }
+  for (int b = threadIdx.x; b < nb; b += blockDim.x)
+    offsets[b] = (b == 0) ? 0 : tot[src][b - 1];   // offsets[E] = valid rows
 }
 
 // One wave places rows [r0, r1) (at most kSteps * 64 rows) in order; cursor[b] (LDS)
@@ -142,11 +139,14 @@ template <int kSteps>
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids, int R, int E,
                                                      int id_bits,
                                                      const int* __restrict__ chunk_base,
+                                                     const int* __restrict__ offsets,
                                                      int* __restrict__ sorted_rows,
                                                      int* __restrict__ row_pos) {
   __shared__ int cursor[kMaxBins];
   const int nb = E + 1;
-  for (int i = lane_id(); i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i];
+  // first position of each bin in this chunk: the chunk's place within the bin plus the
+  // bin's base
+  for (int i = lane_id(); i < nb; i += kWave) cursor[i] = chunk_base[(size_t)blockIdx.x * nb + i] + offsets[i];
   __syncthreads();
   constexpr int chunk = kSteps * kWave;
   const int r0 = blockIdx.x * chunk;
@@ -206,10 +206,10 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
   if (nchunks > 0) {
     if (chunk == kSmallChunk)
       hipLaunchKernelGGL(scatter_kernel<kSmallChunk / kWave>, dim3(nchunks), dim3(64), 0, stream, ids, R, E,
-                         id_bits, chunk_hist, sorted_rows, row_pos);
+                         id_bits, chunk_hist, offsets, sorted_rows, row_pos);
     else
       hipLaunchKernelGGL(scatter_kernel<kChunk / kWave>, dim3(nchunks), dim3(64), 0, stream, ids, R, E, id_bits,
-                         chunk_hist, sorted_rows, row_pos);
+                         chunk_hist, offsets, sorted_rows, row_pos);
   }
   return hipGetLastError();
 }
