@@ -10,10 +10,10 @@
 // Three small launches, no atomics on global memory, deterministic:
 //   1. hist:    one workgroup per chunk of rows (256 rows up to 16384 rows, else
 //               1024), LDS histogram over E+1 bins.
-//   2. scan:    one workgroup; per-bin exclusive scan over chunks (a wave per
-//               bin, lanes over chunks), then the exclusive scan over bins ->
-//               offsets; a chunk's cursor for a bin is its place in the bin plus
-//               the bin's offset.
+//   2. scan:    one workgroup; per-bin exclusive scan over chunks (a thread
+//               per bin), then the exclusive scan over bins -> offsets; a
+//               chunk's cursor for a bin is its place in the bin plus the bin's
+//               offset.
 //   3. scatter: one wave per chunk walks its rows in order, 64 at a time; a
 //               row's rank among equal ids in the same 64 comes from ballots
 //               over the id bits (lanes with equal ids), so ties keep flat
@@ -51,33 +51,32 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, 
   for (int i = threadIdx.x; i < nb; i += blockDim.x) chunk_hist[(size_t)blockIdx.x * nb + i] = h[i];
 }
 
-// One workgroup of 1024 threads.  chunk_hist [nchunks][E+1] becomes, in place, each
-// (chunk, bin)'s first position within its bin (the exclusive scan of the bin's counts
-// over chunks); offsets[b] is the bin's base (the exclusive scan of the bin totals), which
-// the scatter adds.  A wave scans one bin at a time, 64 chunks per step (lanes over
-// chunks, carried from step to step), so the loads of a bin's counts go out together.
-__global__ __launch_bounds__(1024) void scan_kernel(int* __restrict__ chunk_hist, int nchunks,
-                                                    int E, int* __restrict__ offsets) {
+// One workgroup of kScanThreads threads.  chunk_hist [nchunks][E+1] becomes, in place,
+// each (chunk, bin)'s first position within its bin (the exclusive scan of the bin's
+// counts over chunks); offsets[b] is the bin's base (the exclusive scan of the bin
+// totals), which the scatter adds.  A thread scans one bin over the chunks, loading up to
+// kScanBatch chunk counts at once (neighbouring threads read neighbouring bins); a small
+// workgroup leaves each thread the registers for the whole batch.
+constexpr int kScanThreads = 256;
+constexpr int kScanBatch = 64;
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int* __restrict__ chunk_hist, int nchunks,
+                                                            int E, int* __restrict__ offsets) {
   __shared__ int tot[2][kMaxBins + 1];
   const int nb = E + 1;
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  constexpr int kWaves = 1024 / kWave;
-  for (int b = wave; b < nb; b += kWaves) {
-    int carry = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += kWave) {
-      const int c = c0 + lane;
-      const int v = (c < nchunks) ? chunk_hist[(size_t)c * nb + b] : 0;
-      int x = v;   // inclusive scan over the lanes
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    int run = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int v[kScanBatch];
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = (c0 + i < nchunks) ? chunk_hist[(size_t)(c0 + i) * nb + b] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nchunks) chunk_hist[(size_t)(c0 + i) * nb + b] = run;
+        run += v[i];
       }
-      if (c < nchunks) chunk_hist[(size_t)c * nb + b] = carry + x - v;
-      carry += __shfl(x, kWave - 1, kWave);
     }
-    if (lane == 0) tot[0][b] = carry;
+    tot[0][b] = run;
   }
   __syncthreads();
   // Hillis-Steele inclusive scan over the nb bin totals.
@@ -201,7 +200,7 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
   }
   if (nchunks > 0)
     hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, chunk, chunk_hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, chunk_hist, nchunks, E,
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, chunk_hist, nchunks, E,
                      offsets);
   if (nchunks > 0) {
     if (chunk == kSmallChunk)
