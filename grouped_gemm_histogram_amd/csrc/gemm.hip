@@ -150,6 +150,10 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_M_BLOCK
 #define MOE_M_BLOCK 4
 #endif
+// spread the last, partial round of tiles over all XCDs (see the tile loop)
+#ifndef MOE_SPREAD_LAST_ROUND
+#define MOE_SPREAD_LAST_ROUND 1
+#endif
 #ifndef MOE_DECODE_NARROW_ROWS_PER_EXPERT
 #define MOE_DECODE_NARROW_ROWS_PER_EXPERT 2
 #endif
@@ -346,6 +350,23 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   const int total_tiles = kg ? E * mt_all * n_tiles : s_mt_pre[E] * n_tiles;
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (int)((blockIdx.x % 8) * (G / 8) + blockIdx.x / 8) : (int)blockIdx.x;
+  // Tiles go out in rounds of G.  In a full round, XCD x (workgroups b with b % 8 == x)
+  // takes the contiguous tiles [x G/8, (x+1) G/8) of the round.  The last, partial round
+  // of `tail` tiles would fill the first XCDs and leave the others idle; it is cut into
+  // eight contiguous chunks of ceil(tail/8) instead, one per XCD, so that each XCD's L2
+  // serves fewer busy CUs while tiles that share panels still meet in one L2.
+  const int full_rounds = total_tiles / G;
+  const int tail = total_tiles - full_rounds * G;
+  const bool spread = MOE_SPREAD_LAST_ROUND && G % 8 == 0;
+  const int tail_chunk = (tail + 7) / 8;
+  auto tile_at = [&](int r) MOE_INLINE {   // this workgroup's tile of round r, or -1
+    if (r < full_rounds) return r * G + slot;
+    if (r > full_rounds || tail == 0) return -1;
+    if (!spread) return slot < tail ? r * G + slot : -1;
+    const int j = (int)blockIdx.x / 8;
+    const int i = (int)(blockIdx.x % 8) * tail_chunk + j;
+    return (j < tail_chunk && i < tail) ? r * G + i : -1;
+  };
 
   const int K = args.K;
   const int N_out = args.N_out;
@@ -445,7 +466,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 
   int gk = 0;         // slices this workgroup has consumed (selects the direct-load stage)
   bool pre = false;   // bf16: this tile's first slices were issued at the end of the previous one
-  for (int tile = slot; tile < total_tiles; tile += G) {
+  for (int r = 0, tile = tile_at(0); tile >= 0; tile = tile_at(++r)) {
     relane();
     const TileGeo tg = decode(tile);
     const int e = tg.e, seg_end = tg.seg_end, m0 = tg.m0, out_row0 = tg.out_row0, k_bytes = tg.k_bytes;
@@ -703,8 +724,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           // the next tile's geometry and source rows are worked out now, so that the
           // loads of a gathered A's row indices are long done when its first slices
           // are issued at the end of this tile
-          const int tn = tile + G;
-          const bool has_next = tn < total_tiles;
+          const int tn = tile_at(r + 1);
+          const bool has_next = tn >= 0;
           TileGeo nx{};
           uint32_t nA[Cfg::kDmaA], nB[Cfg::kDmaB];
           if (has_next) {
