@@ -57,7 +57,7 @@ moe_status_t check_experts(int32_t E, int32_t k) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct FwdLayout {
-  size_t ids, w, offsets, sorted, rowpos, offws, xp, xps, hf, h, hs, y, total;
+  size_t ids, w, offsets, sorted, rowpos, offws, xp, xps, xpsr, hf, h, hs, y, total;
 };
 
 FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dtype_t w_dtype) {
@@ -80,6 +80,7 @@ FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dt
   L.offws = take(moe::build_offsets_workspace_bytes(R, E));
   L.xp = take(fp8 ? T * H : 0);                     // fp8: quantised token rows
   L.xps = take(fp8 ? T * (H / 128) * 4 : 0);
+  L.xpsr = take(fp8 ? R * (H / 128) * 4 : 0);          // the same scales at the routed rows
   // fp8 at decode sizes: the gate/up GEMM's f32 h, quantised in a second pass
   L.hf = take(fp8 && moe::use_decode_tiles(R, E) ? R * I * 4 : 0);
   L.h = take(R * I * e_act);
@@ -171,11 +172,13 @@ moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t 
 namespace {
 
 // The grouped GEMM with A read directly (a_rows null) or gathered through a_rows.
+// a_scales_by_row (fp8 with a row map): a_scales is [K/128, M_rows], indexed by product row.
 moe_status_t grouped_gemm_impl(const void* A, const float* a_scales, long long A_rows,
                                const int32_t* a_rows, int32_t a_div, const void* B,
                                const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
                                int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
-                               void* C, moe_dtype_t c_dtype, float* c_scales, void* stream) {
+                               void* C, moe_dtype_t c_dtype, float* c_scales, void* stream,
+                               bool a_scales_by_row = false) {
   MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
   MOE_REQUIRE(valid_dtype(ab_dtype) && valid_dtype(c_dtype), "bad dtype");
   MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
@@ -215,6 +218,7 @@ moe_status_t grouped_gemm_impl(const void* A, const float* a_scales, long long A
   p.a_rows = a_rows;
   p.a_div = a_div;
   p.a_total = A_rows;
+  p.a_scales_by_row = a_scales_by_row;
   p.A = A;
   p.a_scales = a_scales;
   p.B = B;
@@ -370,24 +374,30 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   const moe_dtype_t act = fp8 ? MOE_FP8_E4M3 : w_dtype;
   const moe_dtype_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   float* xps = fp8 ? reinterpret_cast<float*>(ws + L.xps) : nullptr;
+  float* xpsr = fp8 ? reinterpret_cast<float*>(ws + L.xpsr) : nullptr;
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
-  // the gate/up GEMM reads token rows through the permutation; the fp8 layer
-  // quantises each token once first
-  if (fp8 && (s = moe_quantize_rows(x, T, H, ws + L.xp, xps, stream))) return s;
+  // The gate/up GEMM reads token rows through the permutation.  The fp8 layer quantises
+  // each token once first and also stores each scale at the token's routed rows
+  // (xpsr [H/128, R], through row_pos), so that a tile of routed rows finds its scales in
+  // consecutive words instead of one cache line per row.
+  if (fp8 && (s = launched(moe::launch_permute_quant(x, (int)T, (int)H, 1, nullptr, nullptr, 0, (int)T, ws + L.xp,
+                                                     xps, as_stream(stream), false, rowpos, k, xpsr, (int)R),
+                           "quantize_rows")))
+    return s;
   if ((s = mark(3))) return s;
   if (fp8 && moe::use_decode_tiles(R, E)) {
     // decode sizes: the small tiles write f32 h (an e4m3 group spans several of them),
     // quantised per row and 128 channels after, with the fused epilogue's arithmetic
     float* hf = reinterpret_cast<float*>(ws + L.hf);
-    if ((s = moe_grouped_gemm_gather(ws + L.xp, xps, T, sorted, k, w13, w13_scales, w_dtype, offs, E, R,
-                                     2 * I, H, MOE_EPI_SILU_MUL, hf, MOE_F32, nullptr, stream)))
+    if ((s = grouped_gemm_impl(ws + L.xp, xpsr, T, sorted, k, w13, w13_scales, w_dtype, offs, E, R, 2 * I, H,
+                               MOE_EPI_SILU_MUL, hf, MOE_F32, nullptr, stream, true)))
       return s;
     if ((s = launched(moe::launch_permute_quant(hf, (int)R, (int)I, 1, nullptr, nullptr, 0, (int)R, ws + L.h, hs,
                                                 as_stream(stream), true),
                       "quantize h")))
       return s;
-  } else if ((s = moe_grouped_gemm_gather(fp8 ? ws + L.xp : x, xps, T, sorted, k, w13, w13_scales, w_dtype,
-                                          offs, E, R, 2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream))) {
+  } else if ((s = grouped_gemm_impl(fp8 ? ws + L.xp : x, xpsr, T, sorted, k, w13, w13_scales, w_dtype, offs, E, R,
+                                    2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream, fp8))) {
     return s;
   }
   if ((s = mark(4))) return s;

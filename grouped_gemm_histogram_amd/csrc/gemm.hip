@@ -93,6 +93,9 @@ struct GemmArgs {
   const int* a_rows;
   int a_div;
   int a_total;
+  // fp8 with a row map and a_scales_by_row set: a_scales is [K/128, M_rows], the scales
+  // already stored at the product rows (consecutive for a tile's rows).
+  int a_scales_by_row;
   // SiLU*up with bf16 operands and C (M-grouped mode): when pre_out is set, also
   // store the f32 pre-activations, gate at column c and up at column N_out + c of
   // pre_out [M_rows, 2 N_out] (rows below offsets[E]; the layer's backward reads them).
@@ -621,10 +624,11 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
         uint32_t sc_off = 0, sc_step = 0;
         if constexpr (Cfg::kLdsScales) {
           if (wave < Cfg::kScaleWaves) {
-            const int r = a_row_of(min(m0 + wave * 64 + lane, args.M_rows - 1));
+            const int pr = min(m0 + wave * 64 + lane, args.M_rows - 1);
+            const int r = args.a_scales_by_row ? pr : a_row_of(pr);
             sc_u = uniform_ptr(reinterpret_cast<const uint8_t*>(args.a_scales));
             sc_off = (uint32_t)r * 4u;
-            sc_step = (uint32_t)args.a_total * 4u;
+            sc_step = (uint32_t)(args.a_scales_by_row ? args.M_rows : args.a_total) * 4u;
           } else {
             const int q = lane < 2 * WN ? lane : 0;
             const int wq = q >> 1, hq = q & 1;
@@ -1202,6 +1206,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.a_rows = p.a_rows;
   a.a_div = p.a_rows ? p.a_div : 1;
   a.a_total = p.a_rows ? (int)p.a_total : (int)p.M_rows;
+  a.a_scales_by_row = (p.a_rows && p.a_scales_by_row) ? 1 : 0;
   if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)

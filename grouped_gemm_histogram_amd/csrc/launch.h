@@ -16,10 +16,13 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
 
 hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
                                const int* offsets, int E, int R, void* xp, hipStream_t stream);
-// sorted_rows and offsets null: row p of xq is token row p, R = T rows; f32_in: x is f32
+// sorted_rows and offsets null: row p of xq is token row p, R = T rows; f32_in: x is f32.
+// Token rows with xs_perm set: each token's scales are also stored at the permuted
+// positions row_pos[t*kslots + j] (j < kslots) of xs_perm [H/128, R_perm].
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
-                                hipStream_t stream, bool f32_in = false);
+                                hipStream_t stream, bool f32_in = false, const int* row_pos = nullptr,
+                                int kslots = 0, float* xs_perm = nullptr, int R_perm = 0);
 
 struct GemmLaunch {
   const void* A;
@@ -46,6 +49,8 @@ struct GemmLaunch {
   const int* a_rows = nullptr;
   int a_div = 1;
   long long a_total = 0;
+  // fp8 with a row map: a_scales indexed by product row ([K/128, M_rows]) instead of by A row
+  bool a_scales_by_row = false;
   // bf16 operands and C, M-grouped mode: SiLU*up also stores the f32 pre-activations
   // [M_rows, 2 N_out] (pre_out)
   float* pre_out = nullptr;

@@ -48,7 +48,9 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const void* __restri
                                                             int H, int k, const int* __restrict__ sorted_rows,
                                                             const int* __restrict__ offsets, int E,
                                                             int R, int nsplit, int units,
-                                                            uint2* __restrict__ xq, float* __restrict__ xs) {
+                                                            uint2* __restrict__ xq, float* __restrict__ xs,
+                                                            const int* __restrict__ row_pos, int kslots,
+                                                            float* __restrict__ xs_perm, int R_perm) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int p = wv / nsplit;
   const int lane = lane_id();
@@ -61,6 +63,15 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const void* __restri
   const uint4* s = static_cast<const uint4*>(x_) + (size_t)src * n8 * (F32IN ? 2 : 1);
   uint2* d = xq + (size_t)p * n8;
   float* sc = xs + p;                         // scales are block-major: [H/128, R]
+  // Token rows (no row map) with xs_perm: each scale is also stored at the permuted
+  // positions of the token's kslots routed rows, xs_perm [H/128, R_perm], so that a
+  // GEMM reading the token rows through the permutation finds a tile's scales in
+  // consecutive words.  Lane j < kslots of each 16-lane group stores slot j's copy.
+  int my_pos = -1;
+  if (xs_perm != nullptr && (lane & 15) < kslots) {
+    const int q = row_pos[(size_t)p * kslots + (lane & 15)];
+    if (q >= 0 && q < R_perm) my_pos = q;
+  }
   for (int base = u_lo; base < u_hi; base += kWave) {
     const int u = base + lane;
     const bool active = u < u_hi;             // whole 16-lane groups, as H % 128 == 0
@@ -94,6 +105,7 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const void* __restri
            (cvt_e4m3x2(clamp448(v[6] / scale), clamp448(v[7] / scale)) << 16);
       d[u] = make_uint2(lo, hi);
       if ((lane & 15) == 0) sc[(size_t)(u / 16) * R] = scale;
+      if (my_pos >= 0) xs_perm[(size_t)(u / 16) * R_perm + my_pos] = scale;
     }
   }
 }
@@ -109,7 +121,8 @@ hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const
 
 hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* sorted_rows,
                                 const int* offsets, int E, int R, void* xq, float* xs,
-                                hipStream_t stream, bool f32_in) {
+                                hipStream_t stream, bool f32_in, const int* row_pos, int kslots,
+                                float* xs_perm, int R_perm) {
   if (R <= 0) return hipSuccess;
   // few rows: split each row over up to ceil(1024 / R) waves of whole 64-lane steps
   const int steps = (H / 8 + kWave - 1) / kWave;
@@ -119,10 +132,12 @@ hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* s
   const long long waves = (long long)R * nsplit;
   if (f32_in)
     hipLaunchKernelGGL(permute_quant_kernel<true>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x,
-                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs);
+                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs,
+                       row_pos, kslots, xs_perm, R_perm);
   else
     hipLaunchKernelGGL(permute_quant_kernel<false>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x,
-                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs);
+                       T, H, k, sorted_rows, offsets, E, R, nsplit, units, static_cast<uint2*>(xq), xs,
+                       row_pos, kslots, xs_perm, R_perm);
   return hipGetLastError();
 }
 
