@@ -260,7 +260,8 @@ typedef struct {
 } moe_aux_t;
 
 /* Bytes of device workspace moe_forward needs (routing arrays, the fp8
- * layer's quantised token rows, h, per-row expert outputs). */
+ * layer's quantised token rows with their scales, by token and by routed row,
+ * h, per-row expert outputs). */
 size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
                              moe_dtype_t w_dtype);
 
