@@ -357,6 +357,108 @@ def test_grouped_gemm_fp8_exact():
     assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
 
 
+# ------------------------------------------------------------------------------------ multi-tile GEMM
+
+def _offsets_from_counts(cnt):
+    off = np.zeros(len(cnt) + 1, np.int32)
+    off[1:] = np.cumsum(cnt)
+    return off
+
+
+@pytest.mark.parametrize("epi", ["none", "silu_mul"])
+def test_grouped_gemm_many_m_tiles(epi):
+    """Experts of 961, 1300 and 2500 rows: 6, 7 and 14 m-tiles of 192 rows, so the tile order's
+    blocks of m-tiles come in several full blocks plus a partial one; compared whole."""
+    cnt = [961, 1300, 2500]
+    off = _offsets_from_counts(cnt)
+    M, E, N, K = int(off[-1]) + 37, 3, 2880, 640
+    say(f"gemm many m-tiles {epi}: M_e={cnt} N={N} K={K}")
+    gen = torch.Generator().manual_seed(41)
+    A = torch.randint(-4, 5, (M, K), generator=gen).to(torch.bfloat16)
+    B = torch.randint(-4, 5, (E, N, K), generator=gen).to(torch.bfloat16)
+    g = ops()
+    if epi == "none":
+        # integer operands: every partial sum is exact in fp32, so the result is bit-exact
+        C = g.grouped_gemm(A.to(DEV), B.to(DEV), torch.from_numpy(off).to(DEV), "none", out_dtype=torch.float32)
+        ref = ogemm.grouped_gemm(A.float().numpy(), B.float().numpy(), off)
+        assert np.array_equal(C.cpu().numpy(), ref.astype(np.float32))
+    else:
+        Bs = (B.float() * 2.0 ** -6).to(torch.bfloat16)        # keeps silu's argument moderate
+        C = g.grouped_gemm(A.to(DEV), Bs.to(DEV), torch.from_numpy(off).to(DEV), "silu_mul")
+        ref = ogemm.grouped_gemm(A.float().numpy(), Bs.float().numpy(), off, "silu_mul")
+        got = np32(C)
+        V = int(off[-1])
+        assert np.all(got[V:] == 0)
+        err = row_rel_err(got[:V], ref[:V])
+        say(f"  err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
+def _exact_fp8(M, E, N, K, seed):
+    gen = torch.Generator().manual_seed(seed)
+    a_codes = e4m3.encode(torch.randint(-4, 5, (M, K), generator=gen).float().numpy())
+    a_s = (2.0 ** torch.randint(-2, 3, (M, K // 128), generator=gen).float()).numpy().astype(np.float32)
+    b_codes = e4m3.encode(torch.randint(-4, 5, (E, N, K), generator=gen).float().numpy())
+    b_s = (2.0 ** torch.randint(-3, 1, (E, N // 128, K // 128), generator=gen).float()).numpy().astype(np.float32)
+    return a_codes, a_s, b_codes, b_s
+
+
+# Launches with more than two rounds of the persistent grid (256 workgroups on MI355X) and
+# many K slices, so workgroups run several tiles each: the cross-tile prefetch and the LDS
+# stage rotation that carries over from one tile to the next are exercised everywhere.
+# Integer operands (fp8: small-integer codes with power-of-two scales) make every partial sum
+# exact in fp32, so the whole output is compared bit for bit, and a rerun must match it.
+MULTI_TILE = [
+    # dtype, gathered, T (token rows), k, E, N, K
+    ("bf16", False, 16384, 1, 32, 1152, 1024),   # 32 x 3 m-tiles x 6 n-tiles = 576 tiles, 16 slices
+    ("bf16", True, 4096, 4, 32, 1152, 1024),
+    ("fp8", False, 16384, 1, 32, 1280, 2048),    # 128x256 tiles: ~32 x 4 x 5 tiles, 16 slices
+    ("fp8", True, 4096, 4, 32, 1280, 2048),
+]
+
+
+@pytest.mark.parametrize("dt,gathered,T,k,E,N,K", MULTI_TILE)
+def test_grouped_gemm_multi_round_exact(dt, gathered, T, k, E, N, K):
+    say(f"gemm multi-round exact {dt} gathered={gathered} T={T} k={k} E={E} N={N} K={K}")
+    R = T * k
+    ids, w, off, sr, rp = _routing(T, E, k, R - 300, 51 + k)
+    V = int(off[-1])
+    g = ops()
+    d_off, d_sr = torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV)
+    if dt == "bf16":
+        gen = torch.Generator().manual_seed(52)
+        A = torch.randint(-4, 5, (T, K), generator=gen).to(torch.bfloat16)
+        B = torch.randint(-4, 5, (E, N, K), generator=gen).to(torch.bfloat16)
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        if gathered:
+            run = lambda: g.grouped_gemm_gather(Ad, Bd, d_off, d_sr, k, "none", out_dtype=torch.float32)
+            ref = ogemm.grouped_gemm(olayer.permute_rows(A.float().numpy(), sr, off, k), B.float().numpy(), off)
+        else:
+            run = lambda: g.grouped_gemm(Ad, Bd, d_off, "none", out_dtype=torch.float32)
+            ref = ogemm.grouped_gemm(A.float().numpy(), B.float().numpy(), off)
+    else:
+        aq, as_, bq, bs = _exact_fp8(T, E, N, K, 53)
+        Ad, Bd = _u8_to_fp8(aq), _u8_to_fp8(bq)
+        d_as = torch.from_numpy(np.ascontiguousarray(as_.T)).to(DEV)
+        d_bs = torch.from_numpy(bs).to(DEV)
+        if gathered:
+            run = lambda: g.grouped_gemm_gather(Ad, Bd, d_off, d_sr, k, "none", a_scales=d_as, b_scales=d_bs,
+                                                out_dtype=torch.float32)
+            ref = ogemm.grouped_gemm(olayer.permute_rows(aq, sr, off, k), bq, off, "none",
+                                     olayer.permute_rows(as_, sr, off, k), bs)
+        else:
+            run = lambda: g.grouped_gemm(Ad, Bd, d_off, "none", a_scales=d_as, b_scales=d_bs,
+                                         out_dtype=torch.float32)
+            ref = ogemm.grouped_gemm(aq, bq, off, "none", as_, bs)
+    C = run()
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    assert np.array_equal(got[:V], ref[:V].astype(np.float32))
+    assert np.all(got[V:] == 0)
+    C2 = run()
+    assert torch.equal(C.cpu().view(torch.int32), C2.cpu().view(torch.int32))
+
+
 # ------------------------------------------------------------------------------------ gathered GEMM
 
 GATHER_CASES = [
