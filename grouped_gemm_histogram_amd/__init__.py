@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     backward,
     backward_workspace_bytes,
     build_offsets,
+    build_offsets_noalloc,
     forward,
     forward_workspace_bytes,
     grouped_gemm,

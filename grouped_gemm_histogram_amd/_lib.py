@@ -42,6 +42,7 @@ SIGNATURES: dict[str, tuple] = {
     "moe_route_topk": (I32, [P, I64, I32, I32, I64, I32, P, P, P]),
     "moe_build_offsets_workspace": (SZ, [I64, I32]),
     "moe_build_offsets": (I32, [P, I64, I32, P, P, P, P, SZ, P]),
+    "moe_build_offsets_noalloc": (I32, [P, I64, I32, P, P, P, P]),
     "moe_permute": (I32, [P, I32, I64, I64, I32, P, P, I32, I64, P, I32, P, P]),
     "moe_grouped_gemm": (I32, [P, P, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P, P]),
     "moe_grouped_gemm_gather": (I32, [P, P, I64, P, I32, P, P, I32, P, I32, I64, I64, I64, I32, P, I32, P,
@@ -67,6 +68,7 @@ class MoeKernels:
     route_topk: Callable
     build_offsets_workspace: Callable
     build_offsets: Callable
+    build_offsets_noalloc: Callable
     permute: Callable
     grouped_gemm: Callable
     grouped_gemm_gather: Callable

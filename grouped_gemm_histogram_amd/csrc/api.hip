@@ -141,6 +141,25 @@ moe_status_t moe_build_offsets(const int32_t* topk_ids, int64_t R, int32_t E, in
                   "build_offsets");
 }
 
+moe_status_t moe_build_offsets_noalloc(const int32_t* topk_ids, int64_t R, int32_t E, int32_t* offsets,
+                                       int32_t* sorted_rows, int32_t* row_pos, void* stream) {
+  MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  MOE_REQUIRE(R >= 0 && R <= kMaxRows, "R=%lld out of range", (long long)R);
+  MOE_REQUIRE(offsets, "offsets is null");
+  MOE_REQUIRE(R == 0 || (topk_ids && sorted_rows && row_pos), "null pointer argument");
+  const size_t need = moe::build_offsets_workspace_bytes(R, E);
+  const size_t cap = moe::build_offsets_noalloc_capacity();
+  if (need > cap)
+    return fail(MOE_ERR_WORKSPACE, "R=%lld, E=%d needs %zu bytes of scratch; the static scratch holds %zu",
+                (long long)R, E, need, cap);
+  void* scratch = nullptr;
+  if (hipError_t e = moe::build_offsets_noalloc_scratch(&scratch))
+    return fail(MOE_ERR_LAUNCH, "static scratch address: %s", hipGetErrorString(e));
+  return launched(moe::launch_build_offsets(topk_ids, (int)R, E, offsets, sorted_rows, row_pos, scratch,
+                                            as_stream(stream)),
+                  "build_offsets_noalloc");
+}
+
 moe_status_t moe_permute(const void* x, moe_dtype_t x_dtype, int64_t T, int64_t H, int32_t k,
                          const int32_t* sorted_rows, const int32_t* offsets, int32_t E, int64_t R,
                          void* x_perm, moe_dtype_t perm_dtype, float* x_perm_scales,

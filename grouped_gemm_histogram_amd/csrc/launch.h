@@ -11,6 +11,9 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, long long
                              int renorm, int* ids, float* weights, hipStream_t stream);
 
 size_t build_offsets_workspace_bytes(long long R, int E);
+// the allocation-free variant's static scratch: its size, and this device's address of it
+size_t build_offsets_noalloc_capacity();
+hipError_t build_offsets_noalloc_scratch(void** out);
 hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int* sorted_rows,
                                 int* row_pos, void* workspace, hipStream_t stream);
 

@@ -20,6 +20,8 @@
 //               order without any atomic.
 // A launch of at most one chunk (decode sizes) runs all three in one workgroup.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -179,6 +181,39 @@ __global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restr
   }
   __syncthreads();
   if (threadIdx.x < kWave) scatter_rows<kChunk / kWave>(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
+}
+
+// Scratch of the allocation-free entry point: one array per GPU, in the code object's
+// device memory, holding the per-chunk histograms that the workspace argument holds
+// otherwise.  Every entry the kernels read is written first by hist_kernel, so nothing
+// needs clearing.  Calls that overlap on one GPU share it and race.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+size_t build_offsets_noalloc_capacity() { return kNoAllocScratchBytes; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+hipError_t build_offsets_noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    // the device address of this GPU's copy (the array's name is a host-side stand-in)
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 size_t build_offsets_workspace_bytes(long long R, int E) {

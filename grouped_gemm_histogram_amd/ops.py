@@ -77,6 +77,21 @@ def build_offsets(topk_ids: torch.Tensor, E: int):
     return offsets, sorted_rows, row_pos
 
 
+def build_offsets_noalloc(topk_ids: torch.Tensor, E: int, offsets: torch.Tensor, sorted_rows: torch.Tensor,
+                          row_pos: torch.Tensor):
+    """build_offsets into caller-provided outputs, with no workspace (the library's static scratch):
+    flat ids int32 [R] -> offsets int32 [E+1], sorted_rows int32 [R], row_pos int32 [R]."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    ids = topk_ids.reshape(-1)
+    R = ids.numel()
+    dev = ids.device
+    _need(offsets, "offsets", torch.int32, (E + 1,), dev)
+    _need(sorted_rows, "sorted_rows", torch.int32, (R,), dev)
+    _need(row_pos, "row_pos", torch.int32, (R,), dev)
+    _check(load().build_offsets_noalloc(_p(ids), R, E, _p(offsets), _p(sorted_rows), _p(row_pos), _stream(ids)))
+    return offsets, sorted_rows, row_pos
+
+
 def permute(x: torch.Tensor, sorted_rows: torch.Tensor, offsets: torch.Tensor, k: int,
             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
             out_scales: Optional[torch.Tensor] = None):

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 
@@ -116,6 +116,25 @@ size_t moe_build_offsets_workspace(int64_t R, int32_t E);
 moe_status_t moe_build_offsets(const int32_t* topk_ids, int64_t R, int32_t E,
                                int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_build_offsets_noalloc -- moe_build_offsets for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as moe_build_offsets, without the workspace: the
+ * kernels' per-chunk histograms live in a static device array inside the
+ * library, 4 MiB per GPU, held from the first call on that GPU until the
+ * process ends.  Calls whose moe_build_offsets_workspace(R, E) exceeds 4 MiB
+ * (e.g. R > ~1M rows at E = 1024) return MOE_ERR_WORKSPACE before launching.
+ * The first call on a GPU looks up that GPU's address of the array (the
+ * stream must belong to the current device, as for every entry point).
+ * Nothing is allocated and nothing in the array needs clearing, but every
+ * call on one GPU uses the same array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+moe_status_t moe_build_offsets_noalloc(const int32_t* topk_ids, int64_t R, int32_t E,
+                                       int32_t* offsets, int32_t* sorted_rows, int32_t* row_pos,
+                                       void* stream);
 
 /*
  * moe_permute -- moves token rows into expert-contiguous order (the

@@ -81,6 +81,9 @@ def test_host_validation(lib):
     assert lib.build_offsets_workspace(65536, 256) >= 64 * 257 * 4
     fake = ctypes.c_void_p(0x1000)
     assert lib.build_offsets(fake, 100, 8, fake, fake, fake, fake, 1, None) == WS
+    # the allocation-free variant refuses sizes beyond its static scratch before any launch
+    assert lib.build_offsets_noalloc(fake, 1 << 21, 1024, fake, fake, fake, None) == WS
+    assert lib.build_offsets_noalloc(fake, 100, 0, fake, fake, fake, None) == INVALID
     # grouped GEMM shape rules
     assert lib.grouped_gemm(fake, None, fake, None, 1, fake, 8, 64, 7, 64, 1, fake, 1, None, None) == INVALID  # odd N
     assert lib.grouped_gemm(fake, None, fake, None, 1, fake, 8, 64, 64, 60, 0, fake, 1, None, None) == INVALID  # K*2 % 16
