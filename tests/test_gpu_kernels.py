@@ -459,6 +459,65 @@ def test_grouped_gemm_multi_round_exact(dt, gathered, T, k, E, N, K):
     assert torch.equal(C.cpu().view(torch.int32), C2.cpu().view(torch.int32))
 
 
+# Launches of one, two and three 64-deep K slices with several tiles per workgroup: the
+# next tile's first slices are issued before the current tile's epilogue, here with fewer
+# slices per tile than LDS stages; E = 63, empty experts (the last among them), experts of
+# exactly 256 and 512 rows, ragged output widths.  Integer operands: bit-exact against the
+# oracle.
+SHORT_K_CASES = [
+    # K, N, epilogue, gathered, E
+    (64, 2304, "none", False, 32),
+    (128, 2304, "silu_mul", False, 32),
+    (192, 2304, "none", True, 32),
+    (64, 1008, "silu_mul", True, 63),
+    (320, 2880, "none", False, 63),
+    (256, 2880, "silu_mul", True, 8),
+]
+
+
+@pytest.mark.parametrize("K,N,epi,gathered,E", SHORT_K_CASES)
+def test_grouped_gemm_short_k_multi_tile(K, N, epi, gathered, E):
+    g = ops()
+    say(f"gemm short K={K} N={N} {epi} gathered={gathered} E={E}")
+    gen = torch.Generator().manual_seed(K + N + E)
+    T, k = (4096, 4) if gathered else (16384, 1)
+    if gathered:
+        ids, w, off, sr, rp = _routing(T, E, k, T * k - 123, K + E)
+    else:
+        # ragged loads summing to at most 16284 rows, with experts of 256 and 512 rows and
+        # empty ones (including the last)
+        wts = np.random.default_rng(E).random(E)
+        wts[:3] = 0
+        wts[E - 1] = 0
+        cnt = np.floor(wts / wts.sum() * (16284 - 768)).astype(np.int64)
+        cnt[0], cnt[1] = 256, 512
+        off = _offsets_from_counts(cnt)
+        assert off[-1] <= 16284
+    V = int(off[-1])
+    A = torch.randint(-3, 4, (T, K), generator=gen).to(torch.bfloat16)
+    B = torch.randint(-3, 4, (E, N, K), generator=gen).to(torch.bfloat16)
+    if epi == "silu_mul":
+        B = (B.float() * 2.0 ** -5).to(torch.bfloat16)
+    d_off = torch.from_numpy(off).to(DEV)
+    odt = torch.float32 if epi == "none" else torch.bfloat16
+    n_out = N // 2 if epi == "silu_mul" else N
+    C = torch.full((T * k, n_out), float("nan"), dtype=odt, device=DEV)
+    if gathered:
+        g.grouped_gemm_gather(A.to(DEV), B.to(DEV), d_off, torch.from_numpy(sr).to(DEV), k, epi, out_dtype=odt, out=C)
+        ref = ogemm.grouped_gemm(olayer.permute_rows(A.float().numpy(), sr, off, k), B.float().numpy(), off, epi)
+    else:
+        g.grouped_gemm(A.to(DEV), B.to(DEV), d_off, epi, out_dtype=odt, out=C)
+        ref = ogemm.grouped_gemm(A.float().numpy(), B.float().numpy(), off, epi)
+    got = np32(C)
+    assert np.all(got[V:] == 0)
+    if epi == "none":
+        assert np.array_equal(got[:V], ref[:V].astype(np.float32))
+    else:
+        err = row_rel_err(got[:V], ref[:V])
+        say(f"  err {err:.3e}")
+        assert err <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------------------------ gathered GEMM
 
 GATHER_CASES = [
