@@ -453,11 +453,13 @@ def main() -> int:
     combine_bytes = V * H * esz + T * H * esz + 8 * T * k
     traffic = load_traffic(cfg.name)
     R = cfg.R
-    pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none", R, E))
+    # moe_forward picks bf16 tiles for the rows that can be valid (V), other dtypes for R
+    tr = V if cfg.dtype == "bf16" else R
+    pred_dn = predicted_mfma_flops(offsets_host, R, H, I, g.grouped_gemm_tile_shape(inp.w13.dtype, "none", max(tr, 1), E))
     # SiLU*up tiles hold tile_n/2 output columns: count them against N_out = I
     # the fp8 layer's gate/up writes e4m3 h (f32 h at decode sizes, quantised after)
     h_dt = torch.float8_e4m3fn if cfg.dtype == "fp8" and R > 8 * E else None
-    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul", R, E, h_dt)
+    tm, tn, ks = g.grouped_gemm_tile_shape(inp.w13.dtype, "silu_mul", max(tr, 1), E, h_dt)
     pred_gu = predicted_mfma_flops(offsets_host, R, I, H, (tm, tn // 2, ks)) * 2
 
     # The dominant kernel's bound: the larger of its MFMA time and its HBM time at peak.

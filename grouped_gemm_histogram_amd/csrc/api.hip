@@ -90,6 +90,27 @@ FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dt
   return L;
 }
 
+// Shape rules of moe_forward that the per-argument checks do not cover: its GEMMs
+// address operands with 32-bit byte offsets, so the gathered token rows, h, and one
+// expert's W13 and W2 must each span under 4 GiB.  nullptr when the shape is accepted.
+const char* forward_shape_error(long long T, long long H, long long I, int E, int k, moe_dtype_t w_dtype) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return "bad E or k";
+  if (!valid_dtype(w_dtype)) return "bad w_dtype";
+  if (T < 0 || H <= 0 || I <= 0 || H > kMaxRows || I > kMaxRows || T * k > kMaxRows) return "bad sizes";
+  const bool fp8 = w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (H % 128 != 0 || I % 128 != 0)) return "fp8 layer needs H and I multiples of 128";
+  if (!fp8 && ((H * esize(w_dtype)) % 16 != 0 || (I * esize(w_dtype)) % 16 != 0))
+    return "H and I rows must be multiples of 16 bytes";
+  const long long e_w = esize(w_dtype);
+  const long long e_act = fp8 ? 1 : e_w;   // gathered token rows (fp8: their e4m3 codes) and h
+  const long long R = T * k;
+  if (T * H * e_act > (long long)UINT32_MAX) return "token rows must span under 4 GiB";
+  if (R * I * e_act > (long long)UINT32_MAX) return "h (T*k rows of I) must span under 4 GiB";
+  if (2 * I * H * e_w > (long long)UINT32_MAX || H * I * e_w > (long long)UINT32_MAX)
+    return "one expert's W13 and W2 must each span under 4 GiB";
+  return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,7 +218,7 @@ moe_status_t grouped_gemm_impl(const void* A, const float* a_scales, long long A
                                const float* b_scales, moe_dtype_t ab_dtype, const int32_t* offsets,
                                int32_t E, int64_t M_rows, int64_t N, int64_t K, moe_epilogue_t epi,
                                void* C, moe_dtype_t c_dtype, float* c_scales, void* stream,
-                               bool a_scales_by_row = false) {
+                               bool a_scales_by_row = false, long long tile_rows = 0) {
   MOE_REQUIRE(E >= 1 && E <= MOE_MAX_EXPERTS, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
   MOE_REQUIRE(valid_dtype(ab_dtype) && valid_dtype(c_dtype), "bad dtype");
   MOE_REQUIRE(epi == MOE_EPI_NONE || epi == MOE_EPI_SILU_MUL, "bad epilogue");
@@ -252,6 +273,7 @@ moe_status_t grouped_gemm_impl(const void* A, const float* a_scales, long long A
   p.C = C;
   p.c_dtype = c_dtype;
   p.c_scales = c_scales;
+  p.tile_rows = tile_rows;
   return launched(moe::launch_grouped_gemm(p, as_stream(stream)), "grouped_gemm");
 }
 
@@ -325,9 +347,7 @@ moe_status_t moe_unpermute_combine(const void* y, moe_dtype_t y_dtype, const int
 
 size_t moe_forward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
                              moe_dtype_t w_dtype) {
-  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK ||
-      !valid_dtype(w_dtype))
-    return 0;
+  if (forward_shape_error(T, H, I, E, k, w_dtype) != nullptr) return 0;   // moe_forward rejects it
   return fwd_layout(T, H, I, E, k, w_dtype).total;
 }
 
@@ -345,13 +365,8 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   MOE_REQUIRE(x_dtype == (w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16),
               "x_dtype must be MOE_F32 for f32 weights and MOE_BF16 otherwise");
   MOE_REQUIRE(out_dtype == MOE_F32 || out_dtype == MOE_BF16, "out_dtype must be MOE_F32 or MOE_BF16");
-  if (fp8) {
-    MOE_REQUIRE(H % 128 == 0 && I % 128 == 0, "fp8 layer needs H and I multiples of 128");
-    MOE_REQUIRE(w13_scales && w2_scales, "fp8 layer needs weight scales");
-  } else {
-    MOE_REQUIRE((H * esize(w_dtype)) % 16 == 0 && (I * esize(w_dtype)) % 16 == 0,
-                "H and I rows must be multiples of 16 bytes");
-  }
+  if (const char* why = forward_shape_error(T, H, I, E, k, w_dtype)) return fail(MOE_ERR_INVALID_ARG, "%s", why);
+  if (fp8) MOE_REQUIRE(w13_scales && w2_scales, "fp8 layer needs weight scales");
   const FwdLayout L = fwd_layout(T, H, I, E, k, w_dtype);
   if (T > 0) {
     MOE_REQUIRE(x && router_logits && w13 && w2 && out, "null pointer argument");
@@ -391,6 +406,11 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
     return ok();
   }
   const moe_dtype_t act = fp8 ? MOE_FP8_E4M3 : w_dtype;
+  // bf16 GEMM tiles are chosen for the rows that can be valid (flat rows past
+  // num_valid_rows are sentinel), known here without reading the offsets; the f32 and fp8
+  // layers keep the choice by routed rows (the fp8 workspace depends on it)
+  const long long V_host = (num_valid_rows >= 0 && num_valid_rows < R) ? num_valid_rows : R;
+  const long long tile_rows = (w_dtype == MOE_BF16) ? (V_host > 0 ? V_host : 1) : R;
   const moe_dtype_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   float* xps = fp8 ? reinterpret_cast<float*>(ws + L.xps) : nullptr;
   float* xpsr = fp8 ? reinterpret_cast<float*>(ws + L.xpsr) : nullptr;
@@ -416,12 +436,12 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
                       "quantize h")))
       return s;
   } else if ((s = grouped_gemm_impl(fp8 ? ws + L.xp : x, xpsr, T, sorted, k, w13, w13_scales, w_dtype, offs, E, R,
-                                    2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream, fp8))) {
+                                    2 * I, H, MOE_EPI_SILU_MUL, ws + L.h, act, hs, stream, fp8, tile_rows))) {
     return s;
   }
   if ((s = mark(4))) return s;
-  if ((s = moe_grouped_gemm(ws + L.h, hs, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
-                            ws + L.y, ydt, nullptr, stream)))
+  if ((s = grouped_gemm_impl(ws + L.h, hs, R, nullptr, 1, w2, w2_scales, w_dtype, offs, E, R, H, I, MOE_EPI_NONE,
+                             ws + L.y, ydt, nullptr, stream, false, tile_rows)))
     return s;
   if ((s = mark(5))) return s;
   if ((s = moe_unpermute_combine(ws + L.y, ydt, rowpos, wts, offs, E, T, H, k, out, out_dtype,

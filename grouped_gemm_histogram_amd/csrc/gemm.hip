@@ -149,9 +149,25 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_DECODE_ROWS_PER_EXPERT
 #define MOE_DECODE_ROWS_PER_EXPERT 8
 #endif
+// bf16 launches of more than that and at most MOE_MID_ROWS_PER_EXPERT rows per expert take
+// mid-size tiles: 32 rows (an expert's rows usually fit one m-tile, so its weights stream
+// once) by 64 weight rows, two waves, six LDS stages, two workgroups per CU (0: no mid tier)
+#ifndef MOE_MID_ROWS_PER_EXPERT
+#define MOE_MID_ROWS_PER_EXPERT 32
+#endif
+#ifndef MOE_TILE_BF16_SILU_MID
+#define MOE_TILE_BF16_SILU_MID 32, 64, 2, 1, 0, 6
+#endif
+#ifndef MOE_TILE_BF16_NONE_MID
+#define MOE_TILE_BF16_NONE_MID 32, 64, 2, 1, 0, 6
+#endif
 // m-tiles per block of an expert's tile order (see the tile decode)
 #ifndef MOE_M_BLOCK
 #define MOE_M_BLOCK 4
+#endif
+// fp8 SiLU*up tiles: split each expert's rows evenly over its m-tiles (see the tile decode)
+#ifndef MOE_EVEN_SPLIT_FP8
+#define MOE_EVEN_SPLIT_FP8 1
 #endif
 // spread the last, partial round of tiles over all XCDs (see the tile loop)
 #ifndef MOE_SPREAD_LAST_ROUND
@@ -320,6 +336,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   };
 
   const bool kg = args.koff != nullptr;   // K-grouped mode (wave-uniform)
+  constexpr bool kEvenSplit = AB == AbType::FP8 && SILU && MOE_EVEN_SPLIT_FP8;
 
   // ---- per-expert m-tile prefix (wave 0, serial per lane + shuffle scan)
   if (wave == 0 && !kg) {
@@ -429,8 +446,18 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       const int within = local - mb * MOE_M_BLOCK * n_tiles;
       nt = within / h;
       ml = mb * MOE_M_BLOCK + (within - nt * h);
-      t.seg_end = off_at(t.e + 1);
-      t.m0 = off_at(t.e) + ml * BM;
+      if (kEvenSplit) {
+        // the expert's rows split evenly over its m-tiles (sizes differ by at most one
+        // row), so that the m-tiles sharing a weight panel stream the same number of lines
+        // and read it in step; rows past a tile's end repeat its last row
+        const int e0 = off_at(t.e);
+        const int m_e = max(off_at(t.e + 1) - e0, 0);
+        t.m0 = e0 + (int)((long long)ml * m_e / mt_e);
+        t.seg_end = e0 + (int)((long long)(ml + 1) * m_e / mt_e);
+      } else {
+        t.seg_end = off_at(t.e + 1);
+        t.m0 = off_at(t.e) + ml * BM;
+      }
       t.out_row0 = t.m0;
       t.k_bytes = K * Tr::kEsize;
       t.b_exp = args.B + (long long)t.e * args.N * ldb_all;
@@ -1147,13 +1174,22 @@ struct TileOf {
 bool use_decode_tiles(long long M_rows, int E) {
   return M_rows <= (long long)MOE_DECODE_ROWS_PER_EXPERT * E;
 }
+bool use_mid_tiles(long long M_rows, int E) {
+  return !use_decode_tiles(M_rows, E) && M_rows <= (long long)MOE_MID_ROWS_PER_EXPERT * E;
+}
 bool use_narrow_decode_tiles(long long M_rows, int E) {
   return M_rows <= (long long)MOE_DECODE_NARROW_ROWS_PER_EXPERT * E;
 }
 
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,
                              int* tile_n, int* k_slice) {
-  if (ab_dtype == 1) {
+  if (ab_dtype == 1 && use_mid_tiles(M_rows, E)) {
+    using M1 = TileOf<MOE_TILE_BF16_SILU_MID>;
+    using M0 = TileOf<MOE_TILE_BF16_NONE_MID>;
+    *tile_m = silu ? M1::kM : M0::kM;
+    *tile_n = silu ? M1::kN : M0::kN;
+    *k_slice = kSliceBytes / 2;
+  } else if (ab_dtype == 1) {
     const bool dec = use_decode_tiles(M_rows, E);
     const bool narrow = use_narrow_decode_tiles(M_rows, E);
     using T1 = TileOf<MOE_TILE_BF16_SILU>;
@@ -1209,13 +1245,24 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.a_scales_by_row = (p.a_rows && p.a_scales_by_row) ? 1 : 0;
   if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
+  // rows the tile shape is chosen for: the launch's rows, or fewer when the caller knows
+  // that only the first tile_rows can be valid
+  const long long trows = (p.tile_rows > 0 && p.tile_rows < p.M_rows) ? p.tile_rows : p.M_rows;
   // dtype: 0 f32, 1 bf16, 2 fp8 (moe_dtype_t values)
-  if (p.ab_dtype == 1 && !p.koff && use_decode_tiles(p.M_rows, p.E)) {
+  if (p.ab_dtype == 1 && !p.koff && use_mid_tiles(trows, p.E)) {
+    if (p.silu) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU_MID>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU_MID>(a, stream);
+    }
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE_MID>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE_MID>(a, stream);
+  }
+  if (p.ab_dtype == 1 && !p.koff && use_decode_tiles(trows, p.E)) {
     if (p.silu) {
       if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
       return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU_DEC>(a, stream);
     }
-    if (use_narrow_decode_tiles(p.M_rows, p.E)) {
+    if (use_narrow_decode_tiles(trows, p.E)) {
       if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE_DEC_NARROW>(a, stream);
       return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE_DEC_NARROW>(a, stream);
     }

@@ -57,6 +57,9 @@ struct GemmLaunch {
   // bf16 operands and C, M-grouped mode: SiLU*up also stores the f32 pre-activations
   // [M_rows, 2 N_out] (pre_out)
   float* pre_out = nullptr;
+  // rows the tile choice assumes (0: M_rows); a caller that knows on the host that only
+  // the first tile_rows rows can be valid passes that count
+  long long tile_rows = 0;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,

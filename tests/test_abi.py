@@ -64,6 +64,9 @@ def test_tile_shape_query(lib):
     assert shape(1, 1, 4, 32)[1] < shape(1, 1, 16384, 32)[1]
     assert shape(2, 1, 4, 32)[1] < shape(2, 1, 16384, 32)[1]
     assert shape(2, 1, 4, 32, c=2)[1] == shape(2, 1, 16384, 32, c=2)[1]
+    # bf16 at 8 to 32 rows per expert: 32-row tiles
+    assert shape(1, 1, 16 * 32, 32)[1] == 32 and shape(1, 0, 32 * 32, 32)[1] == 32
+    assert shape(1, 1, 33 * 32, 32)[1] == 192
     assert lib.grouped_gemm_tile_shape(7, 0, 1, 64, 8, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
     assert lib.grouped_gemm_tile_shape(1, 0, 1, 64, 8, None, ctypes.byref(n), ctypes.byref(k)) == 1
     assert lib.grouped_gemm_tile_shape(1, 0, 1, 64, 0, ctypes.byref(m), ctypes.byref(n), ctypes.byref(k)) == 1
@@ -106,3 +109,10 @@ def test_host_validation(lib):
                        None, fake, 10, None) == WS
     assert lib.forward(fake, 0, fake, fake, None, fake, None, 1, 16, 64, 64, 4, 2, -1, 1, fake, 1,
                        None, fake, 1 << 30, None) == INVALID                                  # x dtype
+    # shapes whose GEMM operands would span 4 GiB or more are refused before any launch, and
+    # have no workspace size: h of T*k = 2^20 rows of I = 4096 bf16 values is 8 GiB
+    assert lib.forward_workspace(1 << 18, 1024, 4096, 8, 4, 1) == 0
+    assert lib.forward(fake, 1, fake, fake, None, fake, None, 1, 1 << 18, 1024, 4096, 8, 4, -1, 1, fake, 1,
+                       None, fake, 1 << 40, None) == INVALID
+    assert b"4 GiB" in lib.last_error()
+    assert lib.forward_workspace(1 << 14, 1024, 4096, 8, 4, 1) > 0                            # 512 MiB of h

@@ -228,12 +228,18 @@ GEMM_CASES = [
     ("bf16", 60, 55, 8, 136, 72, "none"),
     ("bf16", 12, 10, 8, 136, 72, "none"),                     # narrow decode tiles (<= 2 rows/expert)
     ("bf16", 16, 9, 4, 2 * 1408, 384, "silu_mul"),
+    # 8 to 32 rows per expert: the mid-size tiles (32 rows), ragged N and K tails
+    ("bf16", 600, 560, 32, 400, 200, "silu_mul"),
+    ("bf16", 700, 690, 24, 1400, 264, "none"),
+    ("bf16", 2000, 1990, 64, 2 * 456, 712, "silu_mul"),
 ]
 
 
 @pytest.mark.parametrize("dt,M,V,E,N,K,epi", GEMM_CASES)
 def test_grouped_gemm(dt, M, V, E, N, K, epi):
     say(f"gemm {dt} M={M} V={V} E={E} N={N} K={K} {epi}")
+    if dt == "bf16" and 8 * E < M <= 32 * E:
+        assert ops().grouped_gemm_tile_shape(torch.bfloat16, epi, M, E)[0] == 32
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     gen = torch.Generator().manual_seed(M + N + K)
     A = torch.randn(M, K, generator=gen).to(tdt)
