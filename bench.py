@@ -172,11 +172,12 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
     x = f32(inp.x[:S])
     lg = inp.logits[:S].cpu().numpy()
     nv = cfg.num_valid_rows if cfg.num_valid_rows < 0 else min(cfg.num_valid_rows, S * cfg.k)
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=None)
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 0) for i in libs), default=None)
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in libs})) or None
     except Exception:
         pass
     t0 = time.perf_counter()
@@ -184,7 +185,19 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
     dt = time.perf_counter() - t0
     return {"value": S / dt, "unit": "tokens/s", "cores": threads or os.cpu_count(),
             "kind": "oracle", "seconds": dt,
-            "sample": f"first {S} of {cfg.T} tokens, full weights (float64 per-expert loop)"}
+            "sample": f"first {S} of {cfg.T} tokens, full weights (float64 per-expert loop)",
+            "host_cpus": len(os.sched_getaffinity(0)), "blas": blas, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def warm(torch, call, at_least: int, seconds: float) -> int:
@@ -308,7 +321,8 @@ def time_decode(g, torch, cfg, inp, steps: int, tokens=(1, 8, 64)) -> list:
 
 
 def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int, warm_s: float) -> dict:
-    """moe_backward for the forward's routing, timed with HIP events on its stream.
+    """moe_backward for the forward's routing, timed with HIP events on its stream, with f32
+    gradients and again with bf16 gradients (the weight gradients then store half the bytes).
 
     GEMM work: 16*V*H*I flops, of which 4*V*H*I recompute the forward's SiLU*up product
     and 12*V*H*I are the data- and weight-gradient products."""
@@ -316,24 +330,29 @@ def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int, warm_s: floa
                        device="cuda:0").to(torch.bfloat16)
     ws = torch.empty(g.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k), dtype=torch.uint8,
                      device="cuda:0")
-
-    def call():
-        return g.backward(inp.x, inp.w13, inp.w2, dout, aux.topk_weights, aux.offsets, aux.sorted_rows,
-                          aux.row_pos, grad_dtype=torch.float32, workspace=ws)
-    n_warm = warm(torch, call, max(1, warmup), warm_s)
-    ev = HipEvents(2)
-    stream = torch.cuda.current_stream().cuda_stream   # the stream the wrappers queue on
-    ev.record(0, stream)
-    for _ in range(steps):
-        call()
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    ms = ev.ms(0, 1) / steps
-    ev.close()
     V, H, I = cfg.V, cfg.H, cfg.I
-    return {"ms": ms, "steps": steps, "warmup": n_warm, "grad_dtype": "f32", "workspace_bytes": ws.numel(),
-            "gemm_tflops_with_recompute": 16.0 * V * H * I / (ms * 1e-3) / 1e12,
-            "gemm_tflops_gradients_only": 12.0 * V * H * I / (ms * 1e-3) / 1e12}
+    res = {}
+    for name, gdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        def call():
+            return g.backward(inp.x, inp.w13, inp.w2, dout, aux.topk_weights, aux.offsets, aux.sorted_rows,
+                              aux.row_pos, grad_dtype=gdt, workspace=ws)
+        n_warm = warm(torch, call, max(1, warmup), warm_s)
+        ev = HipEvents(2)
+        stream = torch.cuda.current_stream().cuda_stream   # the stream the wrappers queue on
+        ev.record(0, stream)
+        for _ in range(steps):
+            call()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        ms = ev.ms(0, 1) / steps
+        ev.close()
+        res[name] = {"ms": ms, "warmup": n_warm,
+                     "gemm_tflops_with_recompute": 16.0 * V * H * I / (ms * 1e-3) / 1e12,
+                     "gemm_tflops_gradients_only": 12.0 * V * H * I / (ms * 1e-3) / 1e12}
+    return {"ms": res["f32"]["ms"], "steps": steps, "grad_dtype": "f32", "workspace_bytes": ws.numel(),
+            "gemm_tflops_with_recompute": res["f32"]["gemm_tflops_with_recompute"],
+            "gemm_tflops_gradients_only": res["f32"]["gemm_tflops_gradients_only"],
+            "by_grad_dtype": res}
 
 
 def main() -> int:

@@ -24,14 +24,29 @@ expert-contiguous segments:
 
 with silu'(g) = s (1 + g (1 - s)), s = sigmoid(g).  Sentinel rows (permuted
 positions >= offsets[E]) contribute nothing: their dx share, dW terms and
-routing-weight gradient are exactly zero.  bf16/f32 layers only.
+routing-weight gradient are exactly zero.
+
+The fp8 layer (``backward_fp8``): its forward quantises the token rows and h per
+row and 128 channels and uses dequantised block-scaled weights (``oracle.layer``).
+The pages trace a training NaN to that path's backward (the transformers PR
+#45621 write-up, section 3) without fixing its arithmetic; the reading taken is
+the straight-through one used for training through fake quantisation: each
+quantise-then-dequantise step passes gradients unchanged, the weight gradients
+are those of the dequantised weight values, and everything else is the chain
+rule of the forward as it ran, so y and dW2 use the quantised h (h-hat):
+
+    x-hat = dq(q(x)),  gu_p = W13-hat[e] x-hat_t,  h_p = silu(g) * u,  h-hat_p = dq(q(h_p))
+    y_p = W2-hat[e] h-hat_p,   dw[r] = dout[t] . y_p,   dy_p = w[r] dout[t]
+    dh_p = W2-hat[e]^T dy_p (straight through h-hat),   dgu_p as above
+    dx_t = sum over slots of W13-hat[e]^T dgu_p (straight through x-hat)
+    dW2[e] = sum dy_p h-hat_p^T,   dW13[e] = sum dgu_p x-hat_t^T
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .layer import ExpertWeights, permute_rows, silu
+from .layer import ExpertWeights, dequant128, permute_rows, quant128, silu
 from .routing import build_offsets
 
 
@@ -52,8 +67,35 @@ def backward(x, ids, w, W: ExpertWeights, dout) -> dict:
     ``dx_perm`` [V, H], with the routing arrays ``offsets``, ``sorted_rows``,
     ``row_pos``.
     """
-    assert not W.fp8, "the backward covers bf16/f32 layers"
-    x = np.asarray(x, dtype=np.float64)
+    assert not W.fp8, "backward covers bf16/f32 layers; backward_fp8 the fp8 layer"
+    return _backward(np.asarray(x, dtype=np.float64), ids, w, W, dout, None)
+
+
+def backward_fp8(x, ids, w, W: ExpertWeights, dout) -> dict:
+    """Gradients of the fp8 layer (``W.fp8``: e4m3 codes with 128x128 block scales) for
+    fixed routing, straight through the quantisation of x and h (see the module doc).
+
+    ``x`` [T, H] holds the token rows as given to the forward (bf16 values as floats);
+    they are quantised per row and 128 channels here, as the forward does.  ``dw13`` and
+    ``dw2`` are gradients of the dequantised weight values.  Returns the keys of
+    ``backward`` plus ``x_hat`` [T, H] and ``h_hat`` [V, I]; ``h`` is the unquantised h.
+    """
+    assert W.fp8, "backward_fp8 needs block-scaled e4m3 weights"
+    q, s = quant128(np.asarray(x, dtype=np.float32))
+    x_hat = dequant128(q, s)
+
+    def h_round(h):
+        hq, hs = quant128(h.astype(np.float32))   # the forward quantises h from float32
+        return dequant128(hq, hs)
+
+    res = _backward(x_hat, ids, w, W, dout, h_round)
+    res["x_hat"] = x_hat
+    return res
+
+
+def _backward(x, ids, w, W: ExpertWeights, dout, h_round) -> dict:
+    """The chain rule through the per-expert loop; ``h_round`` (or None) maps h to the
+    h the down projection consumes, with the gradient passed straight through it."""
     dout = np.asarray(dout, dtype=np.float64)
     ids = np.asarray(ids)
     T, H = x.shape
@@ -70,6 +112,7 @@ def backward(x, ids, w, W: ExpertWeights, dout) -> dict:
     dy = flat_w[rows][:, None] * dout[tok]               # [V, H]
     gu = np.zeros((V, 2 * I))
     h = np.zeros((V, I))
+    h_hat = np.zeros((V, I))
     y = np.zeros((V, H))
     dgu = np.zeros((V, 2 * I))
     dxp = np.zeros((V, H))
@@ -83,13 +126,14 @@ def backward(x, ids, w, W: ExpertWeights, dout) -> dict:
         gu_e = xp[a:b] @ w13.T
         g, u = gu_e[:, :I], gu_e[:, I:]
         h_e = silu(g) * u
-        gu[a:b], h[a:b] = gu_e, h_e
-        y[a:b] = h_e @ w2.T
+        hh_e = h_e if h_round is None else h_round(h_e)
+        gu[a:b], h[a:b], h_hat[a:b] = gu_e, h_e, hh_e
+        y[a:b] = hh_e @ w2.T
         dh = dy[a:b] @ w2
         dgu[a:b, :I] = dh * u * dsilu(g)
         dgu[a:b, I:] = dh * silu(g)
         dxp[a:b] = dgu[a:b] @ w13
-        dw2[e] = dy[a:b].T @ h_e
+        dw2[e] = dy[a:b].T @ hh_e
         dw13[e] = dgu[a:b].T @ xp[a:b]
 
     dx = np.zeros((T, H))
@@ -101,5 +145,5 @@ def backward(x, ids, w, W: ExpertWeights, dout) -> dict:
         pv = np.where(valid, p, 0)
         dx += np.where(valid[:, None], dxp[pv], 0.0)
         dw[r] = np.where(valid, np.einsum("th,th->t", dout, y[pv]), 0.0)
-    return dict(dx=dx, dw13=dw13, dw2=dw2, dw=dw.reshape(T, k), gu=gu, h=h, y=y, dy=dy, dgu=dgu,
+    return dict(dx=dx, dw13=dw13, dw2=dw2, dw=dw.reshape(T, k), gu=gu, h=h, h_hat=h_hat, y=y, dy=dy, dgu=dgu,
                 dx_perm=dxp, offsets=offsets, sorted_rows=sorted_rows, row_pos=row_pos)
