@@ -54,9 +54,9 @@ SIGNATURES: dict[str, tuple] = {
     "moe_forward_workspace": (SZ, [I64, I64, I64, I32, I32, I32]),
     "moe_forward": (I32, [P, I32, P, P, P, P, P, I32, I64, I64, I64, I32, I32, I64, I32, P, I32,
                           ctypes.POINTER(MoeAux), P, SZ, P]),
-    "moe_backward_workspace": (SZ, [I64, I64, I64, I32, I32]),
-    "moe_backward": (I32, [P, P, P, I32, I64, I64, I64, I32, I32, P, P, P, P, P, P, P, P, I32, P, P, SZ,
-                           P]),
+    "moe_backward_workspace": (SZ, [I64, I64, I64, I32, I32, I32]),
+    "moe_backward": (I32, [P, P, P, P, P, I32, I64, I64, I64, I32, I32, P, P, P, P, P, P, P, P, I32, P, P,
+                           SZ, P]),
     "moe_status_string": (ctypes.c_char_p, [I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (I32, []),

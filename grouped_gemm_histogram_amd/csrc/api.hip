@@ -458,11 +458,11 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
 namespace {
 
 struct BwdLayout {
-  size_t koff, gu, h, dh, dgu, dxp, ones, w13t, w2t, ta, tb, total;
+  size_t koff, gu, h, dh, dgu, dxp, ones, w13t, w2t, ta, tb, xhat, xq, xs, w13hat, w2hat, total;
   long long ldd;   // row stride of the expert-padded transposes (elements)
 };
 
-BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
+BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k, bool fp8) {
   BwdLayout L{};
   const long long R = T * k;
   L.ldd = ((R + 64LL * E) + 63) / 64 * 64;   // >= sum over experts of round_up(M_e, 64)
@@ -483,6 +483,12 @@ BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
   L.w2t = take((size_t)E * H * I * 2);
   L.ta = take((size_t)(H > 2 * I ? H : 2 * I) * L.ldd * 2);
   L.tb = take((size_t)(H > I ? H : I) * L.ldd * 2);
+  // fp8 layer: the dequantised operands (bf16) the backward runs on
+  L.xhat = take(fp8 ? (size_t)T * H * 2 : 0);
+  L.xq = take(fp8 ? (size_t)T * H : 0);
+  L.xs = take(fp8 ? (size_t)T * (H / 128) * 4 : 0);
+  L.w13hat = take(fp8 ? (size_t)E * 2 * I * H * 2 : 0);
+  L.w2hat = take(fp8 ? (size_t)E * H * I * 2 : 0);
   L.total = o;
   return L;
 }
@@ -491,24 +497,30 @@ BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k) {
 
 extern "C" {
 
-size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k) {
-  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
+size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, moe_dtype_t w_dtype) {
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK ||
+      (w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3))
     return 0;
-  return bwd_layout(T, H, I, E, k).total;
+  return bwd_layout(T, H, I, E, k, w_dtype == MOE_FP8_E4M3).total;
 }
 
-moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dtype_t dtype,
-                          int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
-                          const float* topk_weights, const int32_t* offsets,
+moe_status_t moe_backward(const void* x, const void* w13, const float* w13_scales, const void* w2,
+                          const float* w2_scales, moe_dtype_t dtype, int64_t T, int64_t H, int64_t I,
+                          int32_t E, int32_t k, const float* topk_weights, const int32_t* offsets,
                           const int32_t* sorted_rows, const int32_t* row_pos, const void* dout,
                           void* dx, void* dw13, void* dw2, moe_dtype_t grad_dtype,
                           float* dtopk_weights, void* workspace, size_t workspace_bytes,
                           void* stream) {
   if (moe_status_t s = check_experts(E, k)) return s;
-  MOE_REQUIRE(dtype == MOE_BF16, "moe_backward covers bf16 layers (dtype must be MOE_BF16)");
+  MOE_REQUIRE(dtype == MOE_BF16 || dtype == MOE_FP8_E4M3, "dtype must be MOE_BF16 or MOE_FP8_E4M3");
+  const bool fp8 = dtype == MOE_FP8_E4M3;
   MOE_REQUIRE(grad_dtype == MOE_F32 || grad_dtype == MOE_BF16, "grad_dtype must be MOE_F32 or MOE_BF16");
   MOE_REQUIRE(T >= 0 && H > 0 && I > 0 && H % 8 == 0 && I % 8 == 0, "bad sizes (H, I multiples of 8)");
-  const BwdLayout L = bwd_layout(T, H, I, E, k);
+  if (fp8) {
+    MOE_REQUIRE(H % 128 == 0 && I % 128 == 0, "fp8 layer needs H and I multiples of 128");
+    MOE_REQUIRE(w13_scales && w2_scales, "fp8 layer needs weight scales");
+  }
+  const BwdLayout L = bwd_layout(T, H, I, E, k, fp8);
   const long long R = T * k;
   // the transposes and the K-grouped GEMM address rows of ldd elements with 32-bit offsets
   MOE_REQUIRE(R <= kMaxRows / 2 && (2 * I > H ? 2 * I : H) * L.ldd * 2 < 0xffffffffLL &&
@@ -566,10 +578,46 @@ moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dt
     step(moe::launch_fill_f32(static_cast<float*>(dw2), (long long)E * H * I * esize(grad_dtype) / 4, 0.0f, st));
     return launched(e, "backward");
   }
-  // forward intermediates, recomputed: h (bf16) and its pre-activations gu = [g | u]
-  // (f32) from one SiLU*up GEMM reading token rows through the permutation
   step(moe::launch_pad_offsets(offsets, E, (int)R, koff, st));
-  step(gemm(x, w13, R, 2 * I, H, ws + L.h, MOE_BF16, nullptr, 0, 0, E, offsets, sorted_rows, true, gu));
+  if (fp8) {
+    // fp8 layer: the forward's pre-activations gu, recomputed as the forward computed them
+    // (the fp8 grouped GEMM on the token codes and weight codes with fp32 block scaling:
+    // per element the forward's own accumulation), then h-hat = dq(q(silu(g) * u)) with the
+    // forward's arithmetic, so h-hat's codes are the forward's.  The remaining steps run on
+    // the dequantised operands, straight through the quantisers: x-hat, the weights'
+    // block values, and h-hat in place of h.
+    step(moe::launch_permute_quant(x, (int)T, (int)H, 1, nullptr, nullptr, 0, (int)T, ws + L.xq,
+                                   reinterpret_cast<float*>(ws + L.xs), st));
+    moe::GemmLaunch p{};
+    p.A = ws + L.xq;
+    p.a_scales = reinterpret_cast<const float*>(ws + L.xs);
+    p.a_rows = sorted_rows;
+    p.a_div = k;
+    p.a_total = T;
+    p.B = w13;
+    p.b_scales = w13_scales;
+    p.ab_dtype = MOE_FP8_E4M3;
+    p.offsets = offsets;
+    p.E = E;
+    p.M_rows = R;
+    p.N = 2 * I;
+    p.K = H;
+    p.silu = false;
+    p.C = gu;
+    p.c_dtype = MOE_F32;
+    step(moe::launch_grouped_gemm(p, st));
+    step(moe::launch_h_fake_quant(gu, offsets, E, (int)R, (int)I, ws + L.h, st));
+    step(moe::launch_fake_quant_rows(x, T, (int)H, ws + L.xhat, st));
+    step(moe::launch_dequant_blocks(w13, w13_scales, E, (int)(2 * I), (int)H, ws + L.w13hat, st));
+    step(moe::launch_dequant_blocks(w2, w2_scales, E, (int)H, (int)I, ws + L.w2hat, st));
+    x = ws + L.xhat;
+    w13 = ws + L.w13hat;
+    w2 = ws + L.w2hat;
+  } else {
+    // forward intermediates, recomputed: h (bf16) and its pre-activations gu = [g | u]
+    // (f32) from one SiLU*up GEMM reading token rows through the permutation
+    step(gemm(x, w13, R, 2 * I, H, ws + L.h, MOE_BF16, nullptr, 0, 0, E, offsets, sorted_rows, true, gu));
+  }
   // data gradients: dh1 = dout W2 per routed row (on W2^T, dout rows read through the
   // permutation, routing weight not yet applied); then per slot the routing-weight
   // gradient dw = dh1 . h (= dout . y, so y is never recomputed) and the SiLU*up

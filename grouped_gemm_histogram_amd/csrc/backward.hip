@@ -23,6 +23,8 @@
 //                 expert's K range is whole 64-element slices for the weight-gradient
 //                 GEMM and each of its tiles reads a compact block.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -234,6 +236,135 @@ dim3 grid1d(long long n, int per_block) {
   return dim3((unsigned)(b < 1 ? 1 : (b > 65535LL * 32 ? 65535LL * 32 : b)));
 }
 }  // namespace
+
+// ---------------------------------------------------------------- fp8 layer
+//
+// The fp8 layer's backward runs the steps above on dequantised operands, straight
+// through its quantisers: x-hat = dq(q(x)) per token and 128 channels, the weights'
+// dequantised block values, and h-hat = dq(q(h)) per row and 128 channels in place of
+// h (y and dW2 of the fp8 forward use the quantised h).  Codes are decided with the
+// forward's arithmetic (scale = amax / 448, code = RNE(clamp(v / scale)), e4m3) and
+// decoded exactly; the dequantised values are rounded once to bf16.
+
+namespace {
+
+// 8 values of one 128-channel group held by a lane of a 16-lane group -> their
+// quantise-dequantise images, rounded to bf16 (4 packed pairs)
+__device__ __forceinline__ uint4 fake_quant8(const float (&v)[8]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const float scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = cvt_e4m3x2(clamp448(v[2 * i] / scale), clamp448(v[2 * i + 1] / scale));
+    out[i] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8((int)c, 0) * scale,
+                         __builtin_amdgcn_cvt_f32_fp8((int)c, 1) * scale);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+}  // namespace
+
+// x-hat [T, H] from bf16 x [T, H] (H % 128 == 0): one 16-lane group per row and
+// 128-channel group, 8 channels per lane.
+__global__ __launch_bounds__(256) void fake_quant_rows_kernel(const uint4* __restrict__ x, long long groups,
+                                                              uint4* __restrict__ xhat) {
+  const long long gi = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int li = threadIdx.x & 15;
+  const bool ok = gi < groups;
+  float v[8];
+  const uint4 raw = ok ? x[gi * 16 + li] : make_uint4(0, 0, 0, 0);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+  const uint4 o = fake_quant8(v);
+  if (ok) xhat[gi * 16 + li] = o;
+}
+
+// h-hat rows p < offsets[E] of h [R, I] from the f32 pre-activations gu = [g | u]
+// [R, 2I]: h = silu(g) * u (the forward epilogue's function), then quantise-dequantise
+// per 128 channels.  One 16-lane group per row and 128-channel group.
+__global__ __launch_bounds__(256) void h_fake_quant_kernel(const float* __restrict__ gu, const int* __restrict__ offsets,
+                                                           int E, int R, int I, uint4* __restrict__ h) {
+  const long long gi = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int li = threadIdx.x & 15;
+  const int per_row = I / 128;
+  const long long V = min(max(offsets[E], 0), R);
+  const bool ok = gi < V * per_row;
+  const long long p = ok ? gi / per_row : 0;
+  const int c = (int)(ok ? gi - p * per_row : 0) * 128 + li * 8;
+  float v[8];
+  if (ok) {
+    const float4* gp = reinterpret_cast<const float4*>(gu + p * 2 * I + c);
+    const float4* up = reinterpret_cast<const float4*>(gu + p * 2 * I + I + c);
+    const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+    v[0] = silu_mul(g0.x, u0.x); v[1] = silu_mul(g0.y, u0.y); v[2] = silu_mul(g0.z, u0.z); v[3] = silu_mul(g0.w, u0.w);
+    v[4] = silu_mul(g1.x, u1.x); v[5] = silu_mul(g1.y, u1.y); v[6] = silu_mul(g1.z, u1.z); v[7] = silu_mul(g1.w, u1.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  const uint4 o = fake_quant8(v);
+  if (ok) h[(p * I + c) / 8] = o;
+}
+
+// bf16 [E, N, K] from e4m3 codes [E, N, K] and block scales [E, N/128, K/128]
+// (N, K multiples of 128): 8 codes per thread.
+__global__ __launch_bounds__(256) void dequant_blocks_kernel(const uint2* __restrict__ q, const float* __restrict__ s,
+                                                             long long n8, int N, int K, uint4* __restrict__ out) {
+  const int kb = K / 128, nb = N / 128;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
+    const long long el = i * 8;                  // first element: (row = e N + n, k)
+    const long long row = el / K;
+    const int k = (int)(el - row * K);
+    const long long e = row / N;
+    const int n = (int)(row - e * N);
+    const float sc = s[(e * nb + n / 128) * kb + k / 128];
+    const uint2 c = q[i];
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int wv = (int)(j == 0 ? c.x : c.y);
+      o[2 * j] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 0) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 1) * sc);
+      o[2 * j + 1] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 2) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 3) * sc);
+    }
+    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_fake_quant_rows(const void* x, long long T, int H, void* xhat, hipStream_t stream) {
+  const long long groups = T * (H / 128);
+  if (groups == 0) return hipSuccess;
+  const long long blocks = (groups * 16 + 255) / 256;
+  hipLaunchKernelGGL(fake_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(x), groups, static_cast<uint4*>(xhat));
+  return hipGetLastError();
+}
+
+hipError_t launch_h_fake_quant(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream) {
+  const long long groups = (long long)R * (I / 128);
+  if (groups == 0) return hipSuccess;
+  const long long blocks = (groups * 16 + 255) / 256;
+  hipLaunchKernelGGL(h_fake_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, gu, offsets, E, R, I,
+                     static_cast<uint4*>(h));
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_blocks(const void* q, const float* s, int E, int N, int K, void* out, hipStream_t stream) {
+  const long long n8 = (long long)E * N * K / 8;
+  if (n8 == 0) return hipSuccess;
+  const long long blocks = std::min<long long>((n8 + 255) / 256, 65536);
+  hipLaunchKernelGGL(dequant_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint2*>(q), s, n8, N, K, static_cast<uint4*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream) {
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, R, koff);

@@ -80,6 +80,12 @@ hipError_t launch_silu_bwd_route(const float* dh1, const float* gu, const void* 
                                  const int* row_pos, const int* offsets, int E, int R, int I, void* dgu, float* dw,
                                  hipStream_t stream);
 hipError_t launch_fill_f32(float* p, long long n, float v, hipStream_t stream);
+// fp8 layer backward: x-hat = dq(q(x)) per token and 128 channels (bf16 in and out);
+// h-hat rows p < offsets[E] of h [R, I] (bf16) from the f32 pre-activations gu [R, 2I];
+// bf16 [E, N, K] from e4m3 codes with [E, N/128, K/128] block scales
+hipError_t launch_fake_quant_rows(const void* x, long long T, int H, void* xhat, hipStream_t stream);
+hipError_t launch_h_fake_quant(const float* gu, const int* offsets, int E, int R, int I, void* h, hipStream_t stream);
+hipError_t launch_dequant_blocks(const void* q, const float* s, int E, int N, int K, void* out, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, bool y_bf16, const int* row_pos, const float* weights,
                           const int* offsets, int E, int T, int H, int k, void* out, bool out_bf16,

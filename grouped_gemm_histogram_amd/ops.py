@@ -300,24 +300,31 @@ class Gradients:
     dtopk_weights: torch.Tensor   # f32 [T, k]
 
 
-def backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
-    return load().backward_workspace(T, H, I, E, k)
+def backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype = torch.bfloat16) -> int:
+    return load().backward_workspace(T, H, I, E, k, _DT[w_dtype])
 
 
 def backward(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, dout: torch.Tensor,
              topk_weights: torch.Tensor, offsets: torch.Tensor, sorted_rows: torch.Tensor,
              row_pos: torch.Tensor, grad_dtype: torch.dtype = torch.float32,
-             workspace: Optional[torch.Tensor] = None) -> Gradients:
-    """Gradients of the bf16 layer for the routing ``forward`` chose (its aux outputs):
-    x, dout [T, H]; w13 [E, 2I, H]; w2 [E, H, I] -> dx, dw13, dw2 (grad_dtype), dtopk_weights (f32)."""
+             workspace: Optional[torch.Tensor] = None, w13_scale: Optional[torch.Tensor] = None,
+             w2_scale: Optional[torch.Tensor] = None) -> Gradients:
+    """Gradients of the layer for the routing ``forward`` chose (its aux outputs):
+    x, dout bf16 [T, H]; w13 [E, 2I, H]; w2 [E, H, I] (bf16, or e4m3 with block scales
+    w13_scale [E, 2I/128, H/128] and w2_scale [E, H/128, I/128]) -> dx, dw13, dw2
+    (grad_dtype), dtopk_weights (f32)."""
     _need(x, "x", torch.bfloat16)
     T, H = x.shape
     E, I2, _ = w13.shape
     I = I2 // 2
     k = topk_weights.shape[1] if topk_weights.dim() == 2 else 1
     dev = x.device
-    _need(w13, "w13", torch.bfloat16, (E, 2 * I, H), dev)
-    _need(w2, "w2", torch.bfloat16, (E, H, I), dev)
+    _need(w13, "w13", (torch.bfloat16, torch.float8_e4m3fn), (E, 2 * I, H), dev)
+    _need(w2, "w2", w13.dtype, (E, H, I), dev)
+    fp8 = w13.dtype == torch.float8_e4m3fn
+    if fp8:
+        _need(w13_scale, "w13_scale", torch.float32, (E, 2 * I // 128, H // 128), dev)
+        _need(w2_scale, "w2_scale", torch.float32, (E, H // 128, I // 128), dev)
     _need(dout, "dout", torch.bfloat16, (T, H), dev)
     _need(topk_weights, "topk_weights", torch.float32, (T, k), dev)
     _need(offsets, "offsets", torch.int32, (E + 1,), dev)
@@ -330,12 +337,12 @@ def backward(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, dout: torch.T
                   torch.empty(E, H, I, dtype=grad_dtype, device=dev),
                   torch.empty(T, k, dtype=torch.float32, device=dev))
     lib = load()
-    need = lib.backward_workspace(T, H, I, E, k)
+    need = lib.backward_workspace(T, H, I, E, k, _DT[w13.dtype])
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, device=dev)
-    _check(lib.backward(_p(x), _p(w13), _p(w2), _DT[torch.bfloat16], T, H, I, E, k, _p(topk_weights),
-                        _p(offsets), _p(sorted_rows), _p(row_pos), _p(dout), _p(g.dx), _p(g.dw13),
-                        _p(g.dw2), _DT[grad_dtype], _p(g.dtopk_weights), _p(workspace),
-                        workspace.numel(), _stream(x)))
+    _check(lib.backward(_p(x), _p(w13), _p(w13_scale) if fp8 else None, _p(w2), _p(w2_scale) if fp8 else None,
+                        _DT[w13.dtype], T, H, I, E, k, _p(topk_weights), _p(offsets), _p(sorted_rows), _p(row_pos),
+                        _p(dout), _p(g.dx), _p(g.dw13), _p(g.dw2), _DT[grad_dtype], _p(g.dtopk_weights),
+                        _p(workspace), workspace.numel(), _stream(x)))
     return g

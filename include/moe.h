@@ -315,17 +315,18 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace moe_backward needs (recomputed forward
- * intermediates, gradient intermediates, transposed weights and the
- * expert-padded transposed activations).  0 for invalid arguments. */
-size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k);
+ * intermediates, gradient intermediates, transposed weights, the
+ * expert-padded transposed activations, and for w_dtype MOE_FP8_E4M3 the
+ * dequantised operands).  0 for invalid arguments. */
+size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, moe_dtype_t w_dtype);
 
 /*
- * moe_backward -- gradients of the bf16 layer computed by moe_forward, for
- * the routing that forward chose (held fixed).  The pages trace a training
- * NaN to sentinel outputs a kernel left uninitialised ([T45621] section 3):
- * here sentinel rows take no part and every gradient element is written.
- * With p = row_pos[r] the permuted position of routed slot r = t*k + j
- * (valid iff p < offsets[E]) and e its expert:
+ * moe_backward -- gradients of the layer computed by moe_forward, for the
+ * routing that forward chose (held fixed).  The pages trace a training NaN to
+ * sentinel outputs a kernel left uninitialised in the fp8 path's backward
+ * ([T45621] section 3): here sentinel rows take no part and every gradient
+ * element is written.  With p = row_pos[r] the permuted position of routed
+ * slot r = t*k + j (valid iff p < offsets[E]) and e its expert:
  *
  *   dy_p   = w[r] * dout[t]                       (the weight is applied in the combine)
  *   dw[r]  = dout[t] . y_p,   y_p = W2[e] (silu(g) * u),   [g | u] = W13[e] x_t
@@ -334,13 +335,23 @@ size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_
  *   dW2[e] = sum over the expert's rows of dy_p h_p^T
  *   dW13[e] = sum over the expert's rows of dgu_p x_t^T
  *
+ * dtype MOE_FP8_E4M3 (the fp8 layer of moe_forward: e4m3 weights with
+ * [E, N/128, K/128] block scales, token rows and h quantised per row and 128
+ * channels): the same chain rule on the values the forward used, straight
+ * through its quantisers -- x_t is the token row quantised and dequantised,
+ * W13 and W2 are the dequantised weights, and h_p in y_p and dW2 is the
+ * quantised-dequantised h, while dh_p passes to h unchanged; dw13 and dw2 are
+ * the gradients of the dequantised weight values.
+ *
  * The forward's h and pre-activations [g | u] are recomputed here (its SiLU*up
  * grouped GEMM, pre-activations kept in f32); nothing of the forward's workspace
  * is needed.  y_p is not: dw[r] is evaluated as (W2[e]^T dout[t]) . h_p, the same
  * quantity, from the unweighted product W2[e]^T dout[t] that dh_p = w[r] times.
  *
- *   x, w13, w2, dout  MOE_BF16 (dtype must be MOE_BF16): x, dout [T, H];
- *                w13 [E, 2I, H], w2 [E, H, I].  H and I multiples of 8.
+ *   x, dout      bf16 [T, H]: the token rows given to moe_forward.
+ *   w13, w2      [E, 2I, H] and [E, H, I] of dtype (MOE_BF16 or MOE_FP8_E4M3);
+ *                w13_scales [E, 2I/128, H/128] and w2_scales [E, H/128, I/128]
+ *                for fp8 (H, I % 128 == 0), else ignored.  H and I multiples of 8.
  *   topk_weights f32 [T, k], offsets [E+1], sorted_rows [T*k], row_pos [T*k]:
  *                the routing of the forward (moe_aux_t of moe_forward, or
  *                moe_route_topk + moe_build_offsets).
@@ -348,13 +359,14 @@ size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_
  *                MOE_BF16): written in full (tokens with no valid slot and
  *                experts with no rows get exact zeros).
  *   dtopk_weights f32 [T, k]: dw; 0 for sentinel slots.  Nullable.
- *   workspace    >= moe_backward_workspace(T, H, I, E, k) bytes.
+ *   workspace    >= moe_backward_workspace(T, H, I, E, k, dtype) bytes.
  * Accumulation is fp32.  MFMA operands are bf16: dout (the routing weight is
- * applied to the fp32 product), dy rounded once (for dW2), h, dgu and x.
+ * applied to the fp32 product), dy rounded once (for dW2), h, dgu and x (fp8:
+ * the dequantised x, weights and h, each rounded once to bf16).
  */
-moe_status_t moe_backward(const void* x, const void* w13, const void* w2, moe_dtype_t dtype,
-                          int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
-                          const float* topk_weights, const int32_t* offsets,
+moe_status_t moe_backward(const void* x, const void* w13, const float* w13_scales, const void* w2,
+                          const float* w2_scales, moe_dtype_t dtype, int64_t T, int64_t H, int64_t I,
+                          int32_t E, int32_t k, const float* topk_weights, const int32_t* offsets,
                           const int32_t* sorted_rows, const int32_t* row_pos, const void* dout,
                           void* dx, void* dw13, void* dw2, moe_dtype_t grad_dtype,
                           float* dtopk_weights, void* workspace, size_t workspace_bytes,

@@ -184,3 +184,79 @@ def test_backward_full_size():
     say(f"  errors {errs}")
     for key, err in errs.items():
         assert err <= TOL, (key, err)
+
+
+# ----------------------------------------------------------------------------- fp8 layer
+
+FP8_SMALL = [
+    # the DeepSeek-V3-shaped fp8 layer at reduced width, all rows valid and a third valid
+    dict(T=256, H=512, I=256, E=32, nv=-1),
+    dict(T=192, H=384, I=384, E=16, nv=192 * 8 // 3),
+    # decode size: at most 8 routed rows per expert
+    dict(T=6, H=512, I=256, E=32, nv=-1),
+]
+
+
+def _fp8_cfg(T, H, I, E, nv):
+    base = get_config("deepseekv3_fp8")
+    cfg = small_variant(base, T, "_bwd").replace(H=H, I=I, E=E)
+    return cfg.replace(num_valid_rows=nv)
+
+
+def _fp8_weights(inp):
+    return ExpertWeights(HostExperts(inp.w13), HostExperts(inp.w2), inp.w13_scale.cpu().numpy(),
+                         inp.w2_scale.cpu().numpy())
+
+
+def _gpu_backward_fp8(inp, w, off, sr, rp, dout, grad_dtype=torch.float32, x=None):
+    import grouped_gemm_histogram_amd as g
+    T = inp.cfg.T
+    gr = g.backward(inp.x if x is None else x, inp.w13, inp.w2, dout.to(DEV),
+                    torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).reshape(T, -1).to(DEV),
+                    torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(rp).to(DEV),
+                    grad_dtype=grad_dtype, w13_scale=inp.w13_scale, w2_scale=inp.w2_scale)
+    torch.cuda.synchronize()
+    return gr
+
+
+@pytest.mark.parametrize("case", FP8_SMALL, ids=lambda c: f"T{c['T']}-H{c['H']}-I{c['I']}-E{c['E']}-nv{c['nv']}")
+def test_backward_fp8_layers(case):
+    cfg = _fp8_cfg(**case)
+    say(f"backward fp8 {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} nv={cfg.num_valid_rows}")
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dout = _dout(cfg.T, cfg.H, 41)
+    gr = _gpu_backward_fp8(inp, w, off, sr, rp, dout)
+    ref = obwd.backward_fp8(inp.x.float().cpu().numpy(), ids, w, _fp8_weights(inp), dout.float().numpy())
+    errs = {"dx": row_rel_err(np32(gr.dx), ref["dx"]),
+            "dw13": _per_expert(np32(gr.dw13), ref["dw13"]),
+            "dw2": _per_expert(np32(gr.dw2), ref["dw2"]),
+            "dw": row_rel_err(np32(gr.dtopk_weights).reshape(1, -1), ref["dw"].reshape(1, -1))}
+    say(f"  errors {errs}")
+    for key, err in errs.items():
+        assert err <= TOL, (key, err)
+    sentinel = ids >= cfg.E
+    assert np.all(np32(gr.dtopk_weights)[sentinel] == 0)
+    assert np.all(np32(gr.dx)[sentinel.all(axis=1)] == 0)
+    for e in np.flatnonzero(np.diff(off) == 0):
+        assert np.all(np32(gr.dw13)[e] == 0) and np.all(np32(gr.dw2)[e] == 0)
+
+
+def test_backward_fp8_poison_and_determinism():
+    """NaN in the inputs of all-sentinel tokens reaches no gradient; reruns are bitwise equal."""
+    cfg = _fp8_cfg(T=192, H=384, I=384, E=16, nv=192 * 8 // 3)
+    inp = generate(cfg, DEV)
+    ids, w, off, sr, rp = _routing(inp)
+    dead = (ids >= cfg.E).all(axis=1)
+    assert dead.any()
+    dout = _dout(cfg.T, cfg.H, 42)
+    clean = _gpu_backward_fp8(inp, w, off, sr, rp, dout, torch.bfloat16)
+    again = _gpu_backward_fp8(inp, w, off, sr, rp, dout, torch.bfloat16)
+    x_p = inp.x.clone()
+    x_p[torch.from_numpy(dead).to(DEV)] = float("nan")
+    d_p = dout.clone()
+    d_p[torch.from_numpy(dead)] = float("nan")
+    poisoned = _gpu_backward_fp8(inp, w, off, sr, rp, d_p, torch.bfloat16, x=x_p)
+    for f in ("dx", "dw13", "dw2", "dtopk_weights"):
+        assert torch.equal(getattr(clean, f), getattr(again, f)), f
+        assert torch.equal(getattr(clean, f), getattr(poisoned, f)), f
