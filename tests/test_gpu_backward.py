@@ -55,13 +55,20 @@ def _routing(inp):
     return ids, w, off, sr, rp
 
 
-def _gpu_backward(inp, w, off, sr, rp, dout, grad_dtype=torch.float32):
+def _nan_workspace(cfg, w_dtype):
+    """A backward workspace whose every byte is 0xFF (NaN in any float view)."""
+    import grouped_gemm_histogram_amd as g
+    need = g.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, w_dtype)
+    return torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+
+
+def _gpu_backward(inp, w, off, sr, rp, dout, grad_dtype=torch.float32, workspace=None):
     import grouped_gemm_histogram_amd as g
     T = inp.cfg.T
     gr = g.backward(inp.x, inp.w13, inp.w2, dout.to(DEV),
                     torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).reshape(T, -1).to(DEV),
                     torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(rp).to(DEV),
-                    grad_dtype=grad_dtype)
+                    grad_dtype=grad_dtype, workspace=workspace)
     torch.cuda.synchronize()
     return gr
 
@@ -139,7 +146,8 @@ def test_backward_bf16_grads_and_determinism():
 
 
 def test_backward_sentinel_rows_are_poison_proof():
-    """NaN in the inputs of tokens whose slots are all sentinel reaches no gradient."""
+    """NaN in the inputs of tokens whose slots are all sentinel, and a workspace of NaN bytes,
+    reach no gradient."""
     cfg = _cfg("sweep_bf16_v2048")
     inp = generate(cfg, DEV)
     ids, w, off, sr, rp = _routing(inp)
@@ -151,7 +159,8 @@ def test_backward_sentinel_rows_are_poison_proof():
     x_p[torch.from_numpy(dead).to(DEV)] = float("nan")
     d_p = dout.clone()
     d_p[torch.from_numpy(dead)] = float("nan")
-    poisoned = _gpu_backward(inp.__class__(inp.cfg, x_p, inp.logits, inp.w13, inp.w2), w, off, sr, rp, d_p)
+    poisoned = _gpu_backward(inp.__class__(inp.cfg, x_p, inp.logits, inp.w13, inp.w2), w, off, sr, rp, d_p,
+                             workspace=_nan_workspace(cfg, torch.bfloat16))
     for f in ("dx", "dw13", "dw2", "dtopk_weights"):
         assert torch.equal(getattr(clean, f), getattr(poisoned, f)), f
 
@@ -208,13 +217,13 @@ def _fp8_weights(inp):
                          inp.w2_scale.cpu().numpy())
 
 
-def _gpu_backward_fp8(inp, w, off, sr, rp, dout, grad_dtype=torch.float32, x=None):
+def _gpu_backward_fp8(inp, w, off, sr, rp, dout, grad_dtype=torch.float32, x=None, workspace=None):
     import grouped_gemm_histogram_amd as g
     T = inp.cfg.T
     gr = g.backward(inp.x if x is None else x, inp.w13, inp.w2, dout.to(DEV),
                     torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).reshape(T, -1).to(DEV),
                     torch.from_numpy(off).to(DEV), torch.from_numpy(sr).to(DEV), torch.from_numpy(rp).to(DEV),
-                    grad_dtype=grad_dtype, w13_scale=inp.w13_scale, w2_scale=inp.w2_scale)
+                    grad_dtype=grad_dtype, w13_scale=inp.w13_scale, w2_scale=inp.w2_scale, workspace=workspace)
     torch.cuda.synchronize()
     return gr
 
@@ -243,7 +252,8 @@ def test_backward_fp8_layers(case):
 
 
 def test_backward_fp8_poison_and_determinism():
-    """NaN in the inputs of all-sentinel tokens reaches no gradient; reruns are bitwise equal."""
+    """NaN in the inputs of all-sentinel tokens and a workspace of NaN bytes reach no gradient;
+    reruns are bitwise equal."""
     cfg = _fp8_cfg(T=192, H=384, I=384, E=16, nv=192 * 8 // 3)
     inp = generate(cfg, DEV)
     ids, w, off, sr, rp = _routing(inp)
@@ -256,7 +266,8 @@ def test_backward_fp8_poison_and_determinism():
     x_p[torch.from_numpy(dead).to(DEV)] = float("nan")
     d_p = dout.clone()
     d_p[torch.from_numpy(dead)] = float("nan")
-    poisoned = _gpu_backward_fp8(inp, w, off, sr, rp, d_p, torch.bfloat16, x=x_p)
+    poisoned = _gpu_backward_fp8(inp, w, off, sr, rp, d_p, torch.bfloat16, x=x_p,
+                                 workspace=_nan_workspace(cfg, torch.float8_e4m3fn))
     for f in ("dx", "dw13", "dw2", "dtopk_weights"):
         assert torch.equal(getattr(clean, f), getattr(again, f)), f
         assert torch.equal(getattr(clean, f), getattr(poisoned, f)), f
