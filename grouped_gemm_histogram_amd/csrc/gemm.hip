@@ -151,15 +151,16 @@ constexpr int kMaxExperts = 1024;
 #endif
 // bf16 launches of more than that and at most MOE_MID_ROWS_PER_EXPERT rows per expert take
 // mid-size tiles: 32 rows (an expert's rows usually fit one m-tile, so its weights stream
-// once) by 64 weight rows, two waves, six LDS stages, two workgroups per CU (0: no mid tier)
+// once) by 64 weight rows.  SiLU*up: four waves of 16x32 and six LDS stages; down: two waves
+// of 16x64 and four stages (0: no mid tier)
 #ifndef MOE_MID_ROWS_PER_EXPERT
 #define MOE_MID_ROWS_PER_EXPERT 32
 #endif
 #ifndef MOE_TILE_BF16_SILU_MID
-#define MOE_TILE_BF16_SILU_MID 32, 64, 2, 1, 0, 6
+#define MOE_TILE_BF16_SILU_MID 32, 64, 2, 2, 0, 6
 #endif
 #ifndef MOE_TILE_BF16_NONE_MID
-#define MOE_TILE_BF16_NONE_MID 32, 64, 2, 1, 0, 6
+#define MOE_TILE_BF16_NONE_MID 32, 64, 2, 1, 0, 4
 #endif
 // m-tiles per block of an expert's tile order (see the tile decode)
 #ifndef MOE_M_BLOCK
