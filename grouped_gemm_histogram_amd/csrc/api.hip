@@ -458,7 +458,7 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
 namespace {
 
 struct BwdLayout {
-  size_t koff, gu, h, dh, dgu, dxp, ones, w13t, w2t, ta, tb, xhat, xq, xs, w13hat, w2hat, total;
+  size_t koff, gu, h, dh, dgu, dxp, ones, ta, tb, xhat, xq, xs, w13hat, w2hat, total;
   long long ldd;   // row stride of the expert-padded transposes (elements)
 };
 
@@ -479,8 +479,6 @@ BwdLayout bwd_layout(long long T, long long H, long long I, int E, int k, bool f
   L.dgu = take((size_t)R * 2 * I * 2);
   L.dxp = take((size_t)R * H * 4);
   L.ones = take((size_t)R * 4);
-  L.w13t = take((size_t)E * 2 * I * H * 2);
-  L.w2t = take((size_t)E * H * I * 2);
   L.ta = take((size_t)(H > 2 * I ? H : 2 * I) * L.ldd * 2);
   L.tb = take((size_t)(H > I ? H : I) * L.ldd * 2);
   // fp8 layer: the dequantised operands (bf16) the backward runs on
@@ -546,8 +544,9 @@ moe_status_t moe_backward(const void* x, const void* w13, const float* w13_scale
   const int gdt = grad_dtype;
   auto gemm = [&](const void* A, const void* B, long long M, long long N, long long K, void* C, int cdt,
                   const int* kof, long long lda, long long ldb, int nE, const int* offs,
-                  const int* a_rows = nullptr, bool silu = false, float* pre_out = nullptr) {
+                  const int* a_rows = nullptr, bool silu = false, float* pre_out = nullptr, bool b_kn = false) {
     moe::GemmLaunch p{};
+    p.b_kn = b_kn;
     p.a_rows = a_rows;
     p.a_div = k;
     p.a_total = T;
@@ -618,17 +617,16 @@ moe_status_t moe_backward(const void* x, const void* w13, const float* w13_scale
     // (f32) from one SiLU*up GEMM reading token rows through the permutation
     step(gemm(x, w13, R, 2 * I, H, ws + L.h, MOE_BF16, nullptr, 0, 0, E, offsets, sorted_rows, true, gu));
   }
-  // data gradients: dh1 = dout W2 per routed row (on W2^T, dout rows read through the
-  // permutation, routing weight not yet applied); then per slot the routing-weight
-  // gradient dw = dh1 . h (= dout . y, so y is never recomputed) and the SiLU*up
-  // backward of dh = w dh1; dx_perm = dgu W13 (on W13^T).  (The SiLU*up backward stays
-  // a kernel of its own: in the GEMM's epilogue its gu loads stalled every tile.)
-  step(moe::launch_transpose_bf16(w2, E, (int)H, (int)I, ws + L.w2t, st));
-  step(gemm(dout, ws + L.w2t, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets, sorted_rows));
+  // data gradients: dh1 = dout W2 per routed row (W2 [E, H, I] read as [K, N] rows, dout
+  // rows read through the permutation, routing weight not yet applied); then per slot the
+  // routing-weight gradient dw = dh1 . h (= dout . y, so y is never recomputed) and the
+  // SiLU*up backward of dh = w dh1; dx_perm = dgu W13 (W13 [E, 2I, H] read as [K, N]
+  // rows).  (The SiLU*up backward stays a kernel of its own: in the GEMM's epilogue its
+  // gu loads stalled every tile.)
+  step(gemm(dout, w2, R, I, H, dh, MOE_F32, nullptr, 0, 0, E, offsets, sorted_rows, false, nullptr, true));
   step(moe::launch_silu_bwd_route(dh, gu, ws + L.h, topk_weights, row_pos, offsets, E, (int)R, (int)I, ws + L.dgu,
                                   dtopk_weights, st));
-  step(moe::launch_transpose_bf16(w13, E, (int)(2 * I), (int)H, ws + L.w13t, st));
-  step(gemm(ws + L.dgu, ws + L.w13t, R, H, 2 * I, dxp, MOE_F32, nullptr, 0, 0, E, offsets));
+  step(gemm(ws + L.dgu, w13, R, H, 2 * I, dxp, MOE_F32, nullptr, 0, 0, E, offsets, nullptr, false, nullptr, true));
   step(moe::launch_fill_f32(ones, R, 1.0f, st));
   step(moe::launch_combine(dxp, false, row_pos, ones, offsets, E, (int)T, (int)H, k, dx,
                            grad_dtype == MOE_BF16, st));

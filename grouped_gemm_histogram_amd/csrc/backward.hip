@@ -59,8 +59,8 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int* __restrict
   for (int e = threadIdx.x; e <= E; e += blockDim.x) koff[e] = s[src][e];
 }
 
-// Transposes move 64x64 element tiles through LDS with 16-byte global loads and
-// stores (256 threads, two 8-element chunks each way).  In LDS, row r keeps its
+// The segment transposes move 64x64 element tiles through LDS with 16-byte global
+// loads and stores (256 threads, two 8-element chunks each way).  In LDS, row r keeps its
 // 16-byte chunk q at position q ^ ((r >> 3) & 7), so that the column reads of the
 // second phase (lane = (column c, 8-row block b), eight rows 8b..8b+7 of one
 // column) spread over the banks.
@@ -82,33 +82,6 @@ __device__ __forceinline__ uint4 tp_column(const uint16_t* tile, int c, int b) {
 }
 
 }  // namespace
-
-// Batched: dst[b][c][r] = src[b][r][c]; R and C multiples of 8.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
-                                                             uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * 64];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const size_t bz = blockIdx.z;
-  const uint16_t* s = src + bz * (size_t)R * C;
-  uint16_t* d = dst + bz * (size_t)R * C;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int idx = t + 256 * h;            // chunk (row r, chunk q) of the source tile
-    const int r = idx >> 3, q = idx & 7;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + r < R && c0 + 8 * q < C) v = *reinterpret_cast<const uint4*>(s + (size_t)(r0 + r) * C + c0 + 8 * q);
-    *reinterpret_cast<uint4*>(tile + tp_pos(r, q)) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int idx = t + 256 * h;            // output chunk (column c, row block b)
-    const int c = idx >> 3, b = idx & 7;
-    if (c0 + c < C && r0 + 8 * b < R)
-      *reinterpret_cast<uint4*>(d + (size_t)(c0 + c) * R + r0 + 8 * b) = tp_column(tile, c, b);
-  }
-}
 
 // Permuted rows [R, C] -> expert-major transposed blocks: expert e's block is
 // [C, kpad_e] (kpad_e = koff[e+1] - koff[e] = round_up(M_e, 64)) at element
@@ -368,13 +341,6 @@ hipError_t launch_dequant_blocks(const void* q, const float* s, int E, int N, in
 
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream) {
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, R, koff);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream) {
-  if (batch > 0 && R > 0 && C > 0)
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R + 63) / 64, (C + 63) / 64, batch), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(src), R, C, static_cast<uint16_t*>(dst));
   return hipGetLastError();
 }
 

@@ -186,6 +186,12 @@ constexpr int kMaxExperts = 1024;
 // one logical chunk per 16 lanes) reads without bank conflicts on gfx950 in
 // this layout (measured with SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int swz(int row) { return row & 7; }
+// Swizzle of a [K, N] weight tile's k-row (see the kernel's BT mode).  A transposing
+// read takes 4 consecutive k-rows, of which rows r and r + 2 start in the same bank
+// half (128-byte rows); their swizzles differ by 4, which maps the four chunks a lane
+// group reads in one row onto the four chunks the other row leaves free.  Rows r and
+// r + 4 share a swizzle, so the second read of a fragment is the first plus 512 bytes.
+__device__ __forceinline__ int bt_swz(int row) { return (row & 1) | ((row & 2) << 1); }
 
 // One wave-wide direct global->LDS load: lane i's 16 bytes at base + voff land
 // at LDS byte address lds_addr + 16*i (gfx950 global_load_lds_dwordx4; the LDS
@@ -293,10 +299,20 @@ __device__ __forceinline__ int slab_col(int s, int ii) {
   return 4 * SN * (ii >> 2) + 4 * s + (ii & 3);
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
+// BT: B is stored [E][K][N] (row stride ldb = N elements, N contiguous) instead of
+// [E][N][K].  Its LDS tile then holds BNB/64 blocks of 64 columns, each 64 k-rows of
+// 128 bytes (16-byte chunk c of k-row r at chunk c ^ bt_swz(r)), filled by the same
+// 1 KB direct loads (one load: 8 k-rows of one block), and the MFMA weight fragments
+// are read with the transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group,
+// lane 4j + c addresses 4 columns X(c) of k-row j, and lane i receives the k-rows
+// 0..3 of column X(i >> 2) + (i & 3).  Two such reads (k-rows +0..3, +4..7) give a
+// lane the 8 consecutive k of its column that the bf16 MFMA operand holds.
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
   using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
   using Tr = AbTraits<AB>;
+  static_assert(!BT || (AB == AbType::BF16 && !SILU && PF == 0 && BNB % 64 == 0),
+                "B as [K, N] rows: bf16 operands, direct loads, no SiLU, whole 64-column blocks");
   constexpr int THREADS = Cfg::kThreads;
   constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
 
@@ -461,7 +477,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       }
       t.out_row0 = t.m0;
       t.k_bytes = K * Tr::kEsize;
-      t.b_exp = args.B + (long long)t.e * args.N * ldb_all;
+      t.b_exp = args.B + (long long)t.e * (BT ? args.K : args.N) * ldb_all;
       t.lda_b = lda_all;
       t.ldb_b = ldb_all;
     }
@@ -482,6 +498,17 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     }
 #pragma unroll
     for (int j = 0; j < Cfg::kDmaB; ++j) {
+      if constexpr (BT) {
+        // load q fills k-rows 8 (q % 8) + [0, 8) of column block q / 8; lane i the
+        // k-row 8 (q % 8) + i / 8 at physical chunk i % 8.  The k-row's slice offset
+        // and the clamp at K are added at issue (bt_voff).
+        const int q = wave * Cfg::kDmaB + j;
+        const int kr = ((q & 7) << 3) + (lane >> 3);
+        const int lc = (lane & 7) ^ bt_swz(kr);
+        const int col = min(t.n0 + (q >> 3) * 64 + lc * 8, N_out - 8);
+        rb[j] = (uint32_t)kr * t.ldb_b + (uint32_t)col * 2u;
+        continue;
+      }
       const int qrow = (wave * Cfg::kDmaB + j) * 8 + (lane >> 3);
       int half = 0, qq = qrow;
       if constexpr (SILU) {
@@ -678,6 +705,13 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
           for (int j = 0; j < Cfg::kDmaB; ++j) rowB[j] += cc;
         }
+        // BT: offset of load jb's source for slice kt: the lane's k-row kt*64 + kr,
+        // clamped to the last k-row of B (rows past K meet zeroed activations)
+        auto bt_voff = [&](uint32_t rb, int jb, int kt) MOE_INLINE {
+          const int kr = (((wave * Cfg::kDmaB + jb) & 7) << 3) + (lane >> 3);
+          const int over = max(kt * 64 + kr - (K - 1), 0);
+          return rb + (uint32_t)(kt * 64 - over) * ldb_b;
+        };
         auto issue_one = [&](int j, int kt, int stage) MOE_INLINE {
           const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kStageBytes;
           if constexpr (AB == AbType::FP8) {
@@ -696,7 +730,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, a_u, rowA[j] + o);
           else if (j < Cfg::kDmaPerSlice)
             dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + (j - Cfg::kDmaA)) * 1024u, b_u,
-                  rowB[j - Cfg::kDmaA] + o);
+                  BT ? bt_voff(rowB[j - Cfg::kDmaA], j - Cfg::kDmaA, kt) : rowB[j - Cfg::kDmaA] + o);
           else
             dma4(sb + Cfg::kTileBytes + wave_u * 256u, sc_u, sc_off + (uint32_t)kt * sc_step);
         };
@@ -726,16 +760,38 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             const uint8_t* sA = smem[stage];
             const uint8_t* sB = smem[stage] + BM * kSliceBytes;
             const int coff = ((step * 4 + g) ^ rd_swz) << 4;
+            if constexpr (BT) {
+              // lane 16g + 4j + c addresses k-row step*32 + 8g + j, columns X(c) =
+              // the wave's column of MFMA row 4c of subtile s (slab_col keeps each
+              // lane's 4 columns contiguous), and receives its own column's k-rows
+              typedef short v4s __attribute__((ext_vector_type(4)));
+              typedef __attribute__((address_space(3))) v4s lds_v4s;
+              const int jr = (lane & 15) >> 2, cq = lane & 3;
+              const auto lB = (__attribute__((address_space(3))) uint8_t*)sB;
 #pragma unroll
-            for (int s = 0; s < SNB; ++s) {
-              int wrow;
-              if constexpr (SILU) {
-                const int half = s / SNO, ss = s - half * SNO;
-                wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
-              } else {
-                wrow = wn * Cfg::kWNB + 16 * s + ii;
+              for (int s = 0; s < SNB; ++s) {
+                const int X = wn * Cfg::kWNB + slab_col<SNO>(s, 4 * cq);
+                const int off = (X >> 6) * (64 * kSliceBytes) + (step * 32 + 8 * g + jr) * kSliceBytes +
+                                ((((X & 63) >> 3) ^ bt_swz(jr)) << 4) + (X & 7) * 2;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lB + off));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lB + off + 4 * kSliceBytes));
+                fw[s] = make_uint4((uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                                   (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                                   (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                                   (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16));
               }
-              fw[s] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
+            } else {
+#pragma unroll
+              for (int s = 0; s < SNB; ++s) {
+                int wrow;
+                if constexpr (SILU) {
+                  const int half = s / SNO, ss = s - half * SNO;
+                  wrow = half * Cfg::kBNOut + wn * Cfg::kWNOut + 16 * ss + ii;
+                } else {
+                  wrow = wn * Cfg::kWNB + 16 * s + ii;
+                }
+                fw[s] = *reinterpret_cast<const uint4*>(sB + wrow * kSliceBytes + coff);
+              }
             }
             // every subtile is read (its LDS rows always exist); dead ones skip only
             // their MFMAs, so the reads need no exec mask
@@ -832,7 +888,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
                 for (int j = 0; j < Cfg::kDmaA; ++j) dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, na, nA[j] + o);
 #pragma unroll
                 for (int j = 0; j < Cfg::kDmaB; ++j)
-                  dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, nb, nB[j] + o);
+                  dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, nb,
+                        BT ? bt_voff(nB[j], j, s2) : nB[j] + o);
               }
               pre = true;
             }
@@ -1146,12 +1203,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
   using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
   GemmArgs a = a0;
   a.n_tiles = (a.N_out + Cfg::kBNOut - 1) / Cfg::kBNOut;
-  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
+  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF, ST, BT>;
   static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::kThreads, 0) != hipSuccess || n <= 0)
@@ -1236,7 +1293,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.N_out = p.silu ? (int)(p.N / 2) : (int)p.N;
   a.koff = p.koff;
   a.lda = p.koff ? (int)p.lda : (int)p.K;
-  a.ldb = p.koff ? (int)p.ldb : (int)p.K;
+  a.ldb = p.koff ? (int)p.ldb : (p.b_kn ? (int)p.N : (int)p.K);
   if (p.koff && (p.ab_dtype != 1 || p.silu || p.c_dtype == 2)) return hipErrorInvalidValue;
   a.pre_out = p.pre_out;
   if (p.pre_out && (p.ab_dtype != 1 || !p.silu || p.c_dtype != 1 || p.koff)) return hipErrorInvalidValue;
@@ -1246,6 +1303,13 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   a.a_scales_by_row = (p.a_rows && p.a_scales_by_row) ? 1 : 0;
   if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
+  if (p.b_kn) {
+    // B as [E][K][N]: the 192x192 bf16 configuration at every size, no SiLU, M-grouped
+    if (p.ab_dtype != 1 || p.silu || p.koff || p.c_dtype == 2 || p.N % 8 != 0 || p.N < 8)
+      return hipErrorInvalidValue;
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE, true>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE, true>(a, stream);
+  }
   // rows the tile shape is chosen for: the launch's rows, or fewer when the caller knows
   // that only the first tile_rows can be valid
   const long long trows = (p.tile_rows > 0 && p.tile_rows < p.M_rows) ? p.tile_rows : p.M_rows;

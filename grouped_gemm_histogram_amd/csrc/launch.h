@@ -60,6 +60,8 @@ struct GemmLaunch {
   // rows the tile choice assumes (0: M_rows); a caller that knows on the host that only
   // the first tile_rows rows can be valid passes that count
   long long tile_rows = 0;
+  // M-grouped bf16 without SiLU: B stored [E][K][N] (N contiguous) instead of [E][N][K]
+  bool b_kn = false;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream);
 bool grouped_gemm_tile_shape(int ab_dtype, bool silu, int c_dtype, long long M_rows, int E, int* tile_m,
@@ -69,7 +71,6 @@ bool use_decode_tiles(long long M_rows, int E);
 
 // backward steps (backward.hip)
 hipError_t launch_pad_offsets(const int* offsets, int E, int R, int* koff, hipStream_t stream);
-hipError_t launch_transpose_bf16(const void* src, int batch, int R, int C, void* dst, hipStream_t stream);
 // src_rows nullable: row p of the segments is src row src_rows[p] / src_div (of src_total),
 // times src_scale[src_rows[p]] when src_scale is set
 hipError_t launch_transpose_segments_bf16(const void* src, int R, int C, const int* offsets, const int* koff, int E,

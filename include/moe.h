@@ -315,9 +315,9 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace moe_backward needs (recomputed forward
- * intermediates, gradient intermediates, transposed weights, the
- * expert-padded transposed activations, and for w_dtype MOE_FP8_E4M3 the
- * dequantised operands).  0 for invalid arguments. */
+ * intermediates, gradient intermediates, the expert-padded transposed
+ * activations, and for w_dtype MOE_FP8_E4M3 the dequantised operands).  0 for
+ * invalid arguments. */
 size_t moe_backward_workspace(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k, moe_dtype_t w_dtype);
 
 /*
