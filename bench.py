@@ -325,17 +325,19 @@ def time_backward(g, torch, cfg, inp, aux, warmup: int, steps: int, warm_s: floa
     gradients and again with bf16 gradients (the weight gradients then store half the bytes).
 
     GEMM work: 16*V*H*I flops, of which 4*V*H*I recompute the forward's SiLU*up product
-    and 12*V*H*I are the data- and weight-gradient products."""
+    and 12*V*H*I are the data- and weight-gradient products (fp8 layers: the recompute runs
+    on the fp8 codes, the gradient products on the dequantised bf16 values)."""
     dout = torch.randn(cfg.T, cfg.H, generator=torch.Generator(device="cuda:0").manual_seed(7),
                        device="cuda:0").to(torch.bfloat16)
-    ws = torch.empty(g.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k), dtype=torch.uint8,
-                     device="cuda:0")
+    ws = torch.empty(g.backward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, inp.w13.dtype),
+                     dtype=torch.uint8, device="cuda:0")
     V, H, I = cfg.V, cfg.H, cfg.I
     res = {}
     for name, gdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
         def call():
             return g.backward(inp.x, inp.w13, inp.w2, dout, aux.topk_weights, aux.offsets, aux.sorted_rows,
-                              aux.row_pos, grad_dtype=gdt, workspace=ws)
+                              aux.row_pos, grad_dtype=gdt, workspace=ws, w13_scale=inp.w13_scale,
+                              w2_scale=inp.w2_scale)
         n_warm = warm(torch, call, max(1, warmup), warm_s)
         ev = HipEvents(2)
         stream = torch.cuda.current_stream().cuda_stream   # the stream the wrappers queue on
@@ -372,7 +374,7 @@ def main() -> int:
     ap.add_argument("--decode-only", type=int, default=0, metavar="T",
                     help="time only the layer on the first T tokens (decode size) and print that line")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip timing moe_backward (bf16 workloads time it by default)")
+                    help="skip timing moe_backward (bf16 and fp8 workloads time it by default)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -452,7 +454,7 @@ def main() -> int:
         decode = time_decode(g, torch, cfg, inp, args.steps)
 
     backward = None
-    if cfg.dtype == "bf16" and not args.no_backward:
+    if cfg.dtype in ("bf16", "fp8") and not args.no_backward:
         backward = time_backward(g, torch, cfg, inp, aux, args.warmup, args.steps, args.warmup_seconds)
 
     if args.copy_probe:

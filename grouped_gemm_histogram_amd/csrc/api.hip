@@ -520,9 +520,11 @@ moe_status_t moe_backward(const void* x, const void* w13, const float* w13_scale
   }
   const BwdLayout L = bwd_layout(T, H, I, E, k, fp8);
   const long long R = T * k;
-  // the transposes and the K-grouped GEMM address rows of ldd elements with 32-bit offsets
+  // the segment transposes and the K-grouped GEMM address rows of ldd elements with 32-bit
+  // offsets; the other GEMMs address one expert's weights and their A operands (x, dout, dgu)
+  // with 32-bit byte offsets
   MOE_REQUIRE(R <= kMaxRows / 2 && (2 * I > H ? 2 * I : H) * L.ldd * 2 < 0xffffffffLL &&
-                  (long long)E * 2 * I * H <= 0x7fffffffLL,
+                  2 * I * H * 2 <= 0xffffffffLL && T * H * 2 <= 0xffffffffLL && R * 2 * I * 2 <= 0xffffffffLL,
               "sizes exceed the backward's 32-bit addressing");
   MOE_REQUIRE(dx && dw13 && dw2 && w13 && w2, "null pointer argument");
   if (T > 0)

@@ -162,6 +162,14 @@ constexpr int kMaxExperts = 1024;
 #ifndef MOE_TILE_BF16_NONE_MID
 #define MOE_TILE_BF16_NONE_MID 32, 64, 2, 1, 0, 4
 #endif
+// B-as-[K, N] launches (the backward's data-gradient products) of at most this many rows
+// per expert take 128x256 tiles (eight 64x64 waves, three stages)
+#ifndef MOE_BT_SHORT_ROWS_PER_EXPERT
+#define MOE_BT_SHORT_ROWS_PER_EXPERT 384
+#endif
+#ifndef MOE_TILE_BF16_BT_SHORT
+#define MOE_TILE_BF16_BT_SHORT 128, 256, 2, 4, 0, 3
+#endif
 // m-tiles per block of an expert's tile order (see the tile decode)
 #ifndef MOE_M_BLOCK
 #define MOE_M_BLOCK 4
@@ -1304,9 +1312,15 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
   if (p.a_rows && (p.koff || p.a_div < 1 || p.a_total < 1)) return hipErrorInvalidValue;
 
   if (p.b_kn) {
-    // B as [E][K][N]: the 192x192 bf16 configuration at every size, no SiLU, M-grouped
+    // B as [E][K][N], no SiLU, M-grouped: 128x256 tiles at up to 384 rows per expert (an
+    // expert of ~256 rows fills two 128-row m-tiles, where 192-row tiles would run one
+    // third full), else the 192x192 configuration
     if (p.ab_dtype != 1 || p.silu || p.koff || p.c_dtype == 2 || p.N % 8 != 0 || p.N < 8)
       return hipErrorInvalidValue;
+    if (p.M_rows <= (long long)MOE_BT_SHORT_ROWS_PER_EXPERT * p.E) {
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_BT_SHORT, true>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_BT_SHORT, true>(a, stream);
+    }
     if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE, true>(a, stream);
     return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE, true>(a, stream);
   }
