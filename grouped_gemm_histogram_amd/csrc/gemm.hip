@@ -224,8 +224,6 @@ __device__ __forceinline__ void dma4(uint32_t lds_addr, const void* base, uint32
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Wait until at most n slices of PER direct loads each are outstanding (n <= N; vmcnt
 // takes an immediate, so each count has its own instruction).  LGKM: also drain LDS reads.
 template <int PER, int N, bool LGKM>
@@ -531,7 +529,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
   };
 
   int gk = 0;         // slices this workgroup has consumed (selects the direct-load stage)
-  bool pre = false;   // bf16: this tile's first slices were issued at the end of the previous one
   for (int r = 0, tile = tile_at(0); tile >= 0; tile = tile_at(++r)) {
     relane();
     const TileGeo tg = decode(tile);
@@ -540,8 +537,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     const uint32_t lda_b = tg.lda_b, ldb_b = tg.ldb_b;
     const uint8_t* a_src = tg.a_src;
     const uint8_t* b_exp = tg.b_exp;
-    const bool pre_here = pre;
-    pre = false;
 
     // ---- byte offsets of this thread's source rows (A from its base, B from the expert's slab)
     uint32_t a_off[Cfg::kAIters];
@@ -817,23 +812,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
               acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[s]),
                                                                   __builtin_bit_cast(bf16x8, a), acc[t][s], 0, 0, 0);
           };
-          // the next tile's geometry and source rows are worked out now, so that the
-          // loads of a gathered A's row indices are long done when its first slices
-          // are issued at the end of this tile
-          const int tn = tile_at(r + 1);
-          const bool has_next = tn >= 0;
-          TileGeo nx{};
-          uint32_t nA[Cfg::kDmaA], nB[Cfg::kDmaB];
-          if (has_next) {
-            nx = decode(tn);
-            dma_rows(nx, nA, nB);
-          }
+          // Prologue: the tile's first ST-1 slices.  They are issued after the previous
+          // tile's epilogue stores, so waiting for slice 0 needs no wait for those stores
+          // (loads complete in order among themselves).  Issuing them before that
+          // epilogue instead, to overlap its latency, measured 1-2% slower: the wait
+          // then had to cover the stores too.  The stages they land in never hold the
+          // previous tile's last slice, the only one a wave may still be reading.
           uint4 fa0[SM], fw0[SNB], fa1[SM], fw1[SNB];
-          if (pre_here) {
-            // the first slices were issued before the previous tile's epilogue, whose
-            // stores follow them on the counter: wait for everything
-            wait_all_vm();
-          } else {
+          {
             const int npro = min(ST - 1, KT);
             for (int s2 = 0; s2 < npro; ++s2) issue(s2, (st + s2) % ST);
             wait_slices<Cfg::kDmaPerSlice, ST - 2, false>(npro - 1);   // slice 0 has landed
@@ -879,29 +865,6 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           };
           for (int kt = 0; kt + 1 < KT; ++kt) body(kt, std::integral_constant<bool, false>{});
           body(KT - 1, std::integral_constant<bool, true>{});
-          // Cross-tile prefetch: the next tile's first ST-1 slices are issued now, before
-          // this tile's epilogue, so their latency overlaps it.  They land in the stages
-          // of this workgroup's slices gk+KT-ST .. gk+KT-2 (global count), never in that
-          // of the slice just read; every wave finished reading each of them before that
-          // slice's barrier, or, for a slice that is the last of its tile, before the
-          // next tile's first barrier.
-          if (has_next) {
-            if (nx.KT > 0) {
-              const uint8_t* na = uniform_ptr(nx.a_src);
-              const uint8_t* nb = uniform_ptr(nx.b_exp);
-              for (int s2 = 0; s2 < ST - 1 && s2 < nx.KT; ++s2) {
-                const uint32_t o = min((uint32_t)(s2 * kSliceBytes) + cc, (uint32_t)(nx.k_bytes - 16));
-                const uint32_t sb = lds0 + (uint32_t)((gk + KT + s2) % ST) * Cfg::kStageBytes;
-#pragma unroll
-                for (int j = 0; j < Cfg::kDmaA; ++j) dma16(sb + (wave_u * Cfg::kDmaA + j) * 1024u, na, nA[j] + o);
-#pragma unroll
-                for (int j = 0; j < Cfg::kDmaB; ++j)
-                  dma16(sb + BM * kSliceBytes + (wave_u * Cfg::kDmaB + j) * 1024u, nb,
-                        BT ? bt_voff(nB[j], j, s2) : nB[j] + o);
-              }
-              pre = true;
-            }
-          }
           gk += KT;
         } else {
           static_assert(AB == AbType::FP8, "direct loads serve bf16 and fp8");

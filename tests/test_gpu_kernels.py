@@ -410,8 +410,8 @@ def _exact_fp8(M, E, N, K, seed):
 
 
 # Launches with more than two rounds of the persistent grid (256 workgroups on MI355X) and
-# many K slices, so workgroups run several tiles each: the cross-tile prefetch and the LDS
-# stage rotation that carries over from one tile to the next are exercised everywhere.
+# many K slices, so workgroups run several tiles each: the LDS stage rotation that carries
+# over from one tile to the next is exercised everywhere.
 # Integer operands (fp8: small-integer codes with power-of-two scales) make every partial sum
 # exact in fp32, so the whole output is compared bit for bit, and a rerun must match it.
 MULTI_TILE = [
