@@ -289,31 +289,39 @@ __global__ __launch_bounds__(256) void h_fake_quant_kernel(const float* __restri
 }
 
 // bf16 [E, N, K] from e4m3 codes [E, N, K] and block scales [E, N/128, K/128]
-// (N, K multiples of 128).  Each workgroup takes rows of the flattened [E*N, K] code
-// matrix (one row: one expert, one output channel, so one row of scales), its threads
-// 16 codes at a time along the row; no per-element integer division.
+// (N, K multiples of 128).  A workgroup takes kDqRows rows of the flattened [E*N, K] code
+// matrix at a time (a row: one expert and output channel, so one row of scales), each
+// thread 16 codes per row and column step; all of a step's loads are issued before any is
+// converted, so that each thread keeps kDqRows 16-byte loads in flight.
+constexpr int kDqRows = 8;
 __global__ __launch_bounds__(256) void dequant_blocks_kernel(const uint4* __restrict__ q, const float* __restrict__ s,
                                                              long long rows, int N, int K, uint4* __restrict__ out) {
   const int k16 = K / 16, kb = K / 128, nb = N / 128;
-  for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
-    const long long e = row / N;
-    const int n = (int)(row - e * N);
-    const float* srow = s + (e * nb + n / 128) * kb;
-    const uint4* qrow = q + row * k16;
-    uint4* orow = out + row * k16 * 2;
+  for (long long row0 = (long long)blockIdx.x * kDqRows; row0 < rows; row0 += (long long)gridDim.x * kDqRows) {
     for (int c = threadIdx.x; c < k16; c += 256) {
-      const float sc = srow[c >> 3];   // 16 codes at 16c lie in 128-block c / 8
-      const uint4 v = qrow[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[8];
+      uint4 v[kDqRows];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int wv = (int)w[j];
-        o[2 * j] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 0) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 1) * sc);
-        o[2 * j + 1] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 2) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 3) * sc);
+      for (int r = 0; r < kDqRows; ++r)
+        if (row0 + r < rows) v[r] = q[(row0 + r) * k16 + c];
+#pragma unroll
+      for (int r = 0; r < kDqRows; ++r) {
+        const long long row = row0 + r;
+        if (row >= rows) break;
+        const long long e = row / N;
+        const int n = (int)(row - e * N);
+        const float sc = s[(e * nb + n / 128) * kb + (c >> 3)];   // codes 16c.. lie in 128-block c / 8
+        const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int wv = (int)w[j];
+          o[2 * j] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 0) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 1) * sc);
+          o[2 * j + 1] = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(wv, 2) * sc, __builtin_amdgcn_cvt_f32_fp8(wv, 3) * sc);
+        }
+        uint4* orow = out + row * k16 * 2;
+        orow[2 * c] = make_uint4(o[0], o[1], o[2], o[3]);
+        orow[2 * c + 1] = make_uint4(o[4], o[5], o[6], o[7]);
       }
-      orow[2 * c] = make_uint4(o[0], o[1], o[2], o[3]);
-      orow[2 * c + 1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
   }
 }
@@ -339,7 +347,7 @@ hipError_t launch_h_fake_quant(const float* gu, const int* offsets, int E, int R
 hipError_t launch_dequant_blocks(const void* q, const float* s, int E, int N, int K, void* out, hipStream_t stream) {
   const long long rows = (long long)E * N;
   if (rows == 0 || K == 0) return hipSuccess;
-  const long long blocks = std::min<long long>(rows, 65536);
+  const long long blocks = std::min<long long>((rows + kDqRows - 1) / kDqRows, 16384);
   hipLaunchKernelGGL(dequant_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const uint4*>(q), s, rows, N, K, static_cast<uint4*>(out));
   return hipGetLastError();
