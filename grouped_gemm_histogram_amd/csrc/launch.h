@@ -10,6 +10,11 @@ namespace moe {
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, long long valid_rows,
                              int renorm, int* ids, float* weights, hipStream_t stream);
 
+// T*k <= 1024: routing and offsets in one launch (one workgroup of 16 waves, a wave per
+// token at a time); same outputs as launch_route_topk followed by launch_build_offsets.
+hipError_t launch_route_offsets_single(const float* logits, int T, int E, int k, long long valid_rows, int renorm,
+                                       int* ids, float* weights, int* offsets, int* sorted_rows, int* row_pos,
+                                       hipStream_t stream);
 size_t build_offsets_workspace_bytes(long long R, int E);
 // the allocation-free variant's static scratch: its size, and this device's address of it
 size_t build_offsets_noalloc_capacity();

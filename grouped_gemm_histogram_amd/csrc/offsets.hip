@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -154,11 +155,10 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   scatter_rows<kSteps>(ids, r0, min(R, r0 + chunk), E, id_bits, cursor, sorted_rows, row_pos);
 }
 
-// R <= kChunk: histogram, bin scan and scatter in one workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restrict__ ids, int R, int E,
-                                                              int id_bits, int* __restrict__ offsets,
-                                                              int* __restrict__ sorted_rows,
-                                                              int* __restrict__ row_pos) {
+// R <= kChunk: histogram, bin scan and scatter by one workgroup of 1024 threads.
+__device__ __forceinline__ void offsets_single(const int* __restrict__ ids, int R, int E, int id_bits,
+                                               int* __restrict__ offsets, int* __restrict__ sorted_rows,
+                                               int* __restrict__ row_pos) {
   __shared__ int tot[2][kMaxBins + 1];
   const int nb = E + 1;
   for (int b = threadIdx.x; b < nb; b += blockDim.x) tot[0][b] = 0;
@@ -181,6 +181,30 @@ __global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restr
   }
   __syncthreads();
   if (threadIdx.x < kWave) scatter_rows<kChunk / kWave>(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
+}
+
+__global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restrict__ ids, int R, int E,
+                                                              int id_bits, int* __restrict__ offsets,
+                                                              int* __restrict__ sorted_rows,
+                                                              int* __restrict__ row_pos) {
+  offsets_single(ids, R, E, id_bits, offsets, sorted_rows, row_pos);
+}
+
+// Decode sizes (T*k <= kChunk): routing and offsets in one workgroup, one launch instead
+// of two.  The 16 waves route the tokens (a wave per token, as the routing kernel does),
+// then the workgroup builds the offsets from the ids it has just written: the barrier
+// makes a workgroup's global writes visible to its own waves.
+template <int EPL>
+__global__ __launch_bounds__(1024) void route_offsets_single_kernel(const float* __restrict__ logits, int T, int E,
+                                                                    int k, long long valid_rows, int renorm,
+                                                                    int* __restrict__ ids, float* __restrict__ weights,
+                                                                    int id_bits, int* __restrict__ offsets,
+                                                                    int* __restrict__ sorted_rows,
+                                                                    int* __restrict__ row_pos) {
+  for (int t = (int)(threadIdx.x >> 6); t < T; t += (int)(blockDim.x >> 6))
+    route_token<EPL>(logits, t, E, k, valid_rows, renorm, ids, weights);
+  __syncthreads();
+  offsets_single(ids, T * k, E, id_bits, offsets, sorted_rows, row_pos);
 }
 
 // Scratch of the allocation-free entry point: one array per GPU, in the code object's
@@ -245,6 +269,27 @@ hipError_t launch_build_offsets(const int* ids, int R, int E, int* offsets, int*
       hipLaunchKernelGGL(scatter_kernel<kChunk / kWave>, dim3(nchunks), dim3(64), 0, stream, ids, R, E, id_bits,
                          chunk_hist, offsets, sorted_rows, row_pos);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_offsets_single(const float* logits, int T, int E, int k, long long valid_rows, int renorm,
+                                       int* ids, float* weights, int* offsets, int* sorted_rows, int* row_pos,
+                                       hipStream_t stream) {
+  if ((long long)T * k > kChunk || E < 1 || E > kMaxBins - 1) return hipErrorInvalidValue;
+  int id_bits = 1;
+  while ((1 << id_bits) <= E) ++id_bits;   // bins 0..E need id_bits bits
+#define MOE_ROUTE_OFFS_CASE(EPL)                                                                              \
+  hipLaunchKernelGGL(route_offsets_single_kernel<EPL>, dim3(1), dim3(1024), 0, stream, logits, T, E, k,      \
+                     valid_rows, renorm, ids, weights, id_bits, offsets, sorted_rows, row_pos);              \
+  break;
+  switch ((E + kWave - 1) / kWave) {
+    case 1: MOE_ROUTE_OFFS_CASE(1)
+    case 2: MOE_ROUTE_OFFS_CASE(2)
+    case 3: case 4: MOE_ROUTE_OFFS_CASE(4)
+    case 5: case 6: case 7: case 8: MOE_ROUTE_OFFS_CASE(8)
+    default: MOE_ROUTE_OFFS_CASE(16)
+  }
+#undef MOE_ROUTE_OFFS_CASE
   return hipGetLastError();
 }
 

@@ -1,0 +1,83 @@
+// route_device.h -- top-k routing of one token by one wave64, shared by the routing
+// kernel and the one-workgroup routing + offsets kernel of decode sizes.
+//
+// The router picks a small subset of experts for each token ("트랜스포머에서
+// 전문가 혼합 (MoEs)", MoE basics).  Selection is k rounds of a wave-wide
+// arg-max over the token's logits (each lane holds E/64 of them in registers),
+// ordering pairs by (logit descending, expert id ascending); -0.0 and +0.0
+// compare equal.  Weights are a softmax over the k selected logits (or over
+// all E when not renormalising), in fp32.
+#pragma once
+
+#include "device_common.h"
+
+namespace moe {
+
+// Token t's k ids and weights (flat rows t*k .. t*k+k-1; rows at or past valid_rows,
+// when valid_rows >= 0, become sentinel id E with weight 0).  Called by a whole wave.
+template <int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            long long valid_rows, int renorm, int* __restrict__ ids,
+                                            float* __restrict__ weights) {
+  const int lane = lane_id();
+  const float* row = logits + (size_t)t * E;
+
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = (e < E) ? row[e] : 0.0f;
+  }
+
+  uint32_t taken = 0;  // bit i: this lane's logit i already selected
+  float my_val = 0.0f, top = 0.0f;
+  int my_idx = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + kWave * i;
+      // ids grow with i, so a strict '>' keeps the lower id on ties
+      if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (j == 0) top = bv;
+    if (lane == j) {
+      my_val = bv;
+      my_idx = bi;
+    }
+    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi >> 6);
+  }
+
+  const float ex = (lane < k) ? expf(my_val - top) : 0.0f;
+  float denom;
+  if (renorm) {
+    denom = wave_sum(ex);
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i < E) s += expf(v[i] - top);
+    denom = wave_sum(s);
+  }
+  if (lane < k) {
+    const long long r = (long long)t * k + lane;
+    const bool valid = valid_rows < 0 || r < valid_rows;
+    ids[r] = valid ? my_idx : E;
+    weights[r] = valid ? ex / denom : 0.0f;
+  }
+}
+
+}  // namespace moe
