@@ -258,7 +258,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>(lo | (hi << 32));
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool STG = false>
 struct GemmCfg {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kWRows = BM / WM;            // activation rows per wave
@@ -303,16 +303,19 @@ struct GemmCfg {
   // so that the 64 lanes of a store cover whole 128-byte lines.  Written straight from the
   // MFMA layout, a store's 64 pieces of 16 bytes touch ~3 lines in each of 16 rows, and the
   // L1->L2 requests of the partial lines made the weight-gradient stores run at ~3 TB/s.
-  // (fp8 operands keep the direct stores: their down GEMM measured 1.3% slower staged, the
-  // bf16 forward GEMMs were unchanged, the backward's f32 weight gradients 11% faster)
-  static constexpr bool kStagedOut = !SILU && CT != CType::FP8 && AB != AbType::FP8;
+  // One MFMA row group (16 rows) of the wave's block at a time, so that the staging area
+  // always fits in the K loop's stages.  Used by the backward's launches (STG: the
+  // K-grouped weight gradients and the B-as-[K, N] products), whose wide outputs gain
+  // (gradients bit-identical; gpt-oss-20b backward -4% with bf16 and -12% with f32
+  // gradients, DeepSeek-V3 fp8 backward -6%); the forward's GEMMs measured up to 2.7%
+  // slower staged and store directly.
+  static constexpr bool kStagedOut = STG && !SILU && CT != CType::FP8 && AB != AbType::FP8;
   static constexpr int kOutEsize = CT == CType::F32 ? 4 : 2;
   static constexpr int kStgRowBytes = kWNOut * kOutEsize + 16;
-  static constexpr int kStgWaveBytes = kWRows * kStgRowBytes;
+  static constexpr int kStgWaveBytes = 16 * kStgRowBytes;
   static constexpr int kStgChunksPerRow = kWNOut * kOutEsize / 16;
   static_assert(!kStagedOut || (kWNOut * kOutEsize) % 16 == 0, "staged rows are whole 16-byte chunks");
-  static constexpr int kSmemBytes = (kStagedOut && kNW * kStgWaveBytes > ST * kStageBytes) ? kNW * kStgWaveBytes
-                                                                                          : ST * kStageBytes;
+  static_assert(!kStagedOut || kNW * kStgWaveBytes <= ST * kStageBytes, "staging fits in the stages");
 };
 
 // Output column (within the wave's slab) held by MFMA row ii of subtile s.
@@ -329,17 +332,17 @@ __device__ __forceinline__ int slab_col(int s, int ii) {
 // lane 4j + c addresses 4 columns X(c) of k-row j, and lane i receives the k-rows
 // 0..3 of column X(i >> 2) + (i & 3).  Two such reads (k-rows +0..3, +4..7) give a
 // lane the 8 consecutive k of its column that the bf16 MFMA operand holds.
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false,
+          bool STG = false>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST, STG>;
   using Tr = AbTraits<AB>;
   static_assert(!BT || (AB == AbType::BF16 && !SILU && PF == 0 && BNB % 64 == 0),
                 "B as [K, N] rows: bf16 operands, direct loads, no SiLU, whole 64-column blocks");
   constexpr int THREADS = Cfg::kThreads;
   constexpr int SM = Cfg::kSM, SNB = Cfg::kSNB, SNO = Cfg::kSNO;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[Cfg::kSmemBytes];
-  auto smem = reinterpret_cast<uint8_t(*)[Cfg::kStageBytes]>(smem_raw);   // the K loop's stages
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ST][Cfg::kStageBytes];
   __shared__ int s_mt_pre[kMaxExperts + 1];
   __shared__ float s_red[(CT == CType::FP8) ? WN * BM : 1];
 
@@ -1063,42 +1066,68 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
     // ---- epilogue: lane holds columns [cbase, cbase + 4*SNO) of tile row 16*(t*WM+wm) + ii
     relane();
     if constexpr (Cfg::kStagedOut) {
-      // every wave has finished reading the last slice's stage before its block is written
-      __syncthreads();
-      uint8_t* stg = smem_raw + wave * Cfg::kStgWaveBytes;
-      // wave-local row 16 t + ii <-> tile row 16 (t WM + wm) + ii; columns as held
+      if constexpr (SILU && CT == CType::BF16) {
+        // the f32 pre-activations (backward's recompute) keep direct stores
+        if (args.pre_out != nullptr) {
+          const int cb = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
 #pragma unroll
-      for (int t = 0; t < SM; ++t) {
-        uint8_t* srow = stg + (16 * t + ii) * Cfg::kStgRowBytes + 4 * SNO * g * Cfg::kOutEsize;
+          for (int t = 0; t < SM; ++t) {
+            const int rloc = 16 * (t * WM + wm) + ii;
+            if (rloc >= rows_valid) continue;
+            float* pg = args.pre_out + ((long long)out_row0 + rloc) * 2 * N_out + cb;
 #pragma unroll
-        for (int s2 = 0; s2 < SNO; ++s2) {
-          if constexpr (CT == CType::F32) {
-            *reinterpret_cast<float4*>(srow + 16 * s2) =
-                make_float4(acc[t][s2][0], acc[t][s2][1], acc[t][s2][2], acc[t][s2][3]);
-          } else {
-            *reinterpret_cast<uint2*>(srow + 8 * s2) =
-                make_uint2(pack_bf16x2(acc[t][s2][0], acc[t][s2][1]), pack_bf16x2(acc[t][s2][2], acc[t][s2][3]));
+            for (int s2 = 0; s2 < SNO; ++s2)
+              if (cb + 4 * s2 + 4 <= N_out) {
+                *reinterpret_cast<float4*>(pg + 4 * s2) =
+                    make_float4(acc[t][s2][0], acc[t][s2][1], acc[t][s2][2], acc[t][s2][3]);
+                *reinterpret_cast<float4*>(pg + N_out + 4 * s2) = make_float4(
+                    acc[t][SNO + s2][0], acc[t][SNO + s2][1], acc[t][SNO + s2][2], acc[t][SNO + s2][3]);
+              }
           }
         }
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
-      __builtin_amdgcn_wave_barrier();
+      // every wave has finished reading the last slice's stage before its block is written
+      __syncthreads();
+      uint8_t* stg = &smem[0][0] + wave * Cfg::kStgWaveBytes;
       constexpr int CPR = Cfg::kStgChunksPerRow;
-      constexpr int kChunks = Cfg::kWRows * CPR;
+      constexpr int kChunks = 16 * CPR;
       constexpr int kColsPerChunk = 16 / Cfg::kOutEsize;
       const int col0 = n0 + wn * Cfg::kWNOut;
 #pragma unroll
-      for (int q0 = 0; q0 < kChunks; q0 += kWave) {
-        const int q = q0 + lane;
-        if (q < kChunks) {
-          const int lr = q / CPR, cq = q - (q / CPR) * CPR;
-          const int rloc = 16 * ((lr >> 4) * WM + wm) + (lr & 15);
-          const int col = col0 + cq * kColsPerChunk;
-          if (rloc < rows_valid && col + kColsPerChunk <= N_out) {
-            const uint4 val = *reinterpret_cast<const uint4*>(stg + lr * Cfg::kStgRowBytes + cq * 16);
-            *reinterpret_cast<uint4*>(args.C + ((long long)(out_row0 + rloc) * N_out + col) * Cfg::kOutEsize) = val;
+      for (int t = 0; t < SM; ++t) {
+        // row ii of the group: tile row 16 (t WM + wm) + ii; columns as held.  (A wave's
+        // LDS accesses run in order, so the writes of group t+1 follow the reads of t.)
+        uint8_t* srow = stg + ii * Cfg::kStgRowBytes + 4 * SNO * g * Cfg::kOutEsize;
+#pragma unroll
+        for (int s2 = 0; s2 < SNO; ++s2) {
+          float o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o4[r] = SILU ? silu_mul(acc[t][s2][r], acc[t][SNO + s2][r]) : acc[t][s2][r];
+          if constexpr (CT == CType::F32) {
+            *reinterpret_cast<float4*>(srow + 16 * s2) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+          } else {
+            *reinterpret_cast<uint2*>(srow + 8 * s2) =
+                make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
           }
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the group's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        const int rbase = 16 * (t * WM + wm);
+#pragma unroll
+        for (int q0 = 0; q0 < kChunks; q0 += kWave) {
+          const int q = q0 + lane;
+          if (q < kChunks) {
+            const int lr = q / CPR, cq = q - (q / CPR) * CPR;
+            const int rloc = rbase + lr;
+            const int col = col0 + cq * kColsPerChunk;
+            if (rloc < rows_valid && col + kColsPerChunk <= N_out) {
+              const uint4 val = *reinterpret_cast<const uint4*>(stg + lr * Cfg::kStgRowBytes + cq * 16);
+              *reinterpret_cast<uint4*>(args.C + ((long long)(out_row0 + rloc) * N_out + col) * Cfg::kOutEsize) = val;
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
       }
       // the next tile's first loads land in the stages this block overlays
       __syncthreads();
@@ -1233,12 +1262,13 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false>
+template <AbType AB, CType CT, bool SILU, int BM, int BNB, int WM, int WN, int PF, int ST, bool BT = false,
+          bool STG = false>
 hipError_t launch_cfg(const GemmArgs& a0, hipStream_t stream) {
-  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST>;
+  using Cfg = GemmCfg<AB, CT, SILU, BM, BNB, WM, WN, PF, ST, STG>;
   GemmArgs a = a0;
   a.n_tiles = (a.N_out + Cfg::kBNOut - 1) / Cfg::kBNOut;
-  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF, ST, BT>;
+  auto kern = grouped_gemm_kernel<AB, CT, SILU, BM, BNB, WM, WN, PF, ST, BT, STG>;
   static const int per_cu = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, Cfg::kThreads, 0) != hipSuccess || n <= 0)
@@ -1340,11 +1370,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
     if (p.ab_dtype != 1 || p.silu || p.koff || p.c_dtype == 2 || p.N % 8 != 0 || p.N < 8)
       return hipErrorInvalidValue;
     if (p.M_rows <= (long long)MOE_BT_SHORT_ROWS_PER_EXPERT * p.E) {
-      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_BT_SHORT, true>(a, stream);
-      return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_BT_SHORT, true>(a, stream);
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_BT_SHORT, true, true>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_BT_SHORT, true, true>(a, stream);
     }
-    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE, true>(a, stream);
-    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE, true>(a, stream);
+    if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE, true, true>(a, stream);
+    return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE, true, true>(a, stream);
   }
   // rows the tile shape is chosen for: the launch's rows, or fewer when the caller knows
   // that only the first tile_rows can be valid
@@ -1374,6 +1404,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& p, hipStream_t stream) {
     if (p.silu) {
       if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, true, MOE_TILE_BF16_SILU>(a, stream);
       return launch_cfg<AbType::BF16, CType::F32, true, MOE_TILE_BF16_SILU>(a, stream);
+    }
+    if (p.koff) {   // the backward's weight gradients: staged stores
+      if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE, false, true>(a, stream);
+      return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE, false, true>(a, stream);
     }
     if (p.c_dtype == 1) return launch_cfg<AbType::BF16, CType::BF16, false, MOE_TILE_BF16_NONE>(a, stream);
     return launch_cfg<AbType::BF16, CType::F32, false, MOE_TILE_BF16_NONE>(a, stream);
