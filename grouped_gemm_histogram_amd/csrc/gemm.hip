@@ -728,12 +728,15 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
 #pragma unroll
           for (int j = 0; j < Cfg::kDmaB; ++j) rowB[j] += cc;
         }
-        // BT: offset of load jb's source for slice kt: the lane's k-row kt*64 + kr,
-        // clamped to the last k-row of B (rows past K meet zeroed activations)
+        // BT: offset of load jb's source for slice kt: the lane's k-row kt*KS + kr (KS bf16
+        // k-rows per slice), clamped to the last k-row of B (rows past K meet zeroed
+        // activations).  rb already holds kr * ldb_b, so the clamp adds (kt*KS - over) rows,
+        // which may be negative for K < KS; the unsigned arithmetic wraps to the right offset.
         auto bt_voff = [&](uint32_t rb, int jb, int kt) MOE_INLINE {
+          constexpr int KS = kSliceBytes / 2;
           const int kr = (((wave * Cfg::kDmaB + jb) & 7) << 3) + (lane >> 3);
-          const int over = max(kt * 64 + kr - (K - 1), 0);
-          return rb + (uint32_t)(kt * 64 - over) * ldb_b;
+          const int over = max(kt * KS + kr - (K - 1), 0);
+          return rb + (uint32_t)(kt * KS - over) * ldb_b;
         };
         auto issue_one = [&](int j, int kt, int stage) MOE_INLINE {
           const uint32_t sb = lds0 + (uint32_t)stage * Cfg::kStageBytes;
