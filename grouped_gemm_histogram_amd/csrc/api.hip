@@ -40,6 +40,9 @@ int esize(moe_dtype_t d) { return d == MOE_F32 ? 4 : (d == MOE_BF16 ? 2 : 1); }
 bool valid_dtype(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_FP8_E4M3; }
 
 constexpr long long kMaxRows = 0x7fffffffLL;
+// fp8 layers of at least this many routed rows copy the token scales to the routed
+// positions with a separate gather pass (see moe_forward)
+constexpr long long kGatherScalesMinRows = 4096;
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -430,11 +433,20 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
   float* hs = fp8 ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
   // The gate/up GEMM reads token rows through the permutation.  The fp8 layer quantises
   // each token once first and also stores each scale at the token's routed rows
-  // (xpsr [H/128, R], through row_pos), so that a tile of routed rows finds its scales in
-  // consecutive words instead of one cache line per row.
+  // (xpsr [H/128, R]), so that a tile of routed rows finds its scales in consecutive
+  // words instead of one cache line per row.  With many rows a second pass gathers them
+  // along the routed positions (the quantising kernel's per-slot stores would touch one
+  // cache line per scale); with few, the quantising kernel stores them through row_pos
+  // and saves a launch.
+  const bool gather_sc = fp8 && R >= kGatherScalesMinRows;
   if (fp8 && (s = launched(moe::launch_permute_quant(x, (int)T, (int)H, 1, nullptr, nullptr, 0, (int)T, ws + L.xp,
-                                                     xps, as_stream(stream), false, rowpos, k, xpsr, (int)R),
+                                                     xps, as_stream(stream), false, gather_sc ? nullptr : rowpos,
+                                                     gather_sc ? 0 : k, gather_sc ? nullptr : xpsr, (int)R),
                            "quantize_rows")))
+    return s;
+  if (gather_sc && (s = launched(moe::launch_gather_scales(xps, (int)T, (int)(H / 128), sorted, k, offs, E, (int)R,
+                                                           xpsr, as_stream(stream)),
+                                 "gather scales")))
     return s;
   if ((s = mark(3))) return s;
   if (fp8 && moe::use_decode_tiles(R, E)) {

@@ -1136,6 +1136,32 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
       __syncthreads();
     } else {
     const int cbase = n0 + wn * Cfg::kWNOut + 4 * SNO * g;
+    // fp8 output: the scale of each row's 128 columns needs the amax over the WN waves
+    // that hold them; every row group's partial amax goes through LDS at once, so that
+    // a tile's epilogue takes two barriers instead of two per row group
+    [[maybe_unused]] float fp8_scale[SM];
+    if constexpr (CT == CType::FP8) {
+#pragma unroll
+      for (int t = 0; t < SM; ++t) {
+        float am = 0.f;
+#pragma unroll
+        for (int s = 0; s < SNO; ++s)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(silu_mul(acc[t][s][r], acc[t][SNO + s][r])));
+        am = fmaxf(am, __shfl_xor(am, 16, 64));
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        if (g == 0) s_red[wn * BM + 16 * (t * WM + wm) + ii] = am;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < SM; ++t) {
+        float amax = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, s_red[w2 * BM + 16 * (t * WM + wm) + ii]);
+        fp8_scale[t] = (amax == 0.f) ? 1.f : amax / 448.f;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int t = 0; t < SM; ++t) {
       const int rloc = 16 * (t * WM + wm) + ii;
@@ -1149,18 +1175,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           v[4 * s + r] = SILU ? silu_mul(acc[t][s][r], acc[t][SNO + s][r]) : acc[t][s][r];
 
       if constexpr (CT == CType::FP8) {
-        float am = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4 * SNO; ++i) am = fmaxf(am, fabsf(v[i]));
-        am = fmaxf(am, __shfl_xor(am, 16, 64));
-        am = fmaxf(am, __shfl_xor(am, 32, 64));
-        if (g == 0) s_red[wn * BM + rloc] = am;
-        __syncthreads();
-        float amax = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < WN; ++w2) amax = fmaxf(amax, s_red[w2 * BM + rloc]);
-        __syncthreads();
-        const float scale = (amax == 0.f) ? 1.f : amax / 448.f;
+        const float scale = fp8_scale[t];
         if (row_ok && cbase + 4 * SNO <= N_out) {
           uint32_t wd[SNO];
 #pragma unroll

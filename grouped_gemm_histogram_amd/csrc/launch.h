@@ -31,6 +31,11 @@ hipError_t launch_permute_quant(const void* x, int T, int H, int k, const int* s
                                 const int* offsets, int E, int R, void* xq, float* xs,
                                 hipStream_t stream, bool f32_in = false, const int* row_pos = nullptr,
                                 int kslots = 0, float* xs_perm = nullptr, int R_perm = 0);
+// xs_perm [G, R] at routed position p < offsets[E] = xs [G, T] of the row's token
+// (sorted_rows[p] / k): the token scales copied to the permuted positions by a gather,
+// coalesced along p, instead of the quantising kernel's per-slot stores.
+hipError_t launch_gather_scales(const float* xs, int T, int G, const int* sorted_rows, int k,
+                                const int* offsets, int E, int R, float* xs_perm, hipStream_t stream);
 
 struct GemmLaunch {
   const void* A;

@@ -110,6 +110,29 @@ __global__ __launch_bounds__(256) void permute_quant_kernel(const void* __restri
   }
 }
 
+// One thread per routed position and a share of the scale groups: reads the
+// position's token (one word), then that token's scale of each group it covers
+// (the [G, T] table is a few MB and stays in L2) and writes them along p.
+__global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ xs, int T, int G,
+                                                            const int* __restrict__ sorted_rows, int k,
+                                                            const int* __restrict__ offsets, int E, int R,
+                                                            float* __restrict__ xs_perm) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= R || p >= offsets[E]) return;
+  const int t = sorted_rows[p] / k;
+  if (t < 0 || t >= T) return;   // inconsistent permutation: leave the position unwritten
+  for (int g = blockIdx.y; g < G; g += gridDim.y) xs_perm[(size_t)g * R + p] = xs[(size_t)g * T + t];
+}
+
+hipError_t launch_gather_scales(const float* xs, int T, int G, const int* sorted_rows, int k,
+                                const int* offsets, int E, int R, float* xs_perm, hipStream_t stream) {
+  if (R <= 0 || G <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((R + 255) / 256), (unsigned)(G < 8 ? G : 8));
+  hipLaunchKernelGGL(gather_scales_kernel, grid, dim3(256), 0, stream, xs, T, G, sorted_rows, k, offsets, E, R,
+                     xs_perm);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute_copy(const void* x, int T, int row_bytes, int k, const int* sorted_rows,
                                const int* offsets, int E, int R, void* xp, hipStream_t stream) {
   if (R > 0)
