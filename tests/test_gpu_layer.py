@@ -105,6 +105,32 @@ def test_layer_sentinel_poison():
     assert torch.equal(out[~dead].view(torch.int16), base[~dead].view(torch.int16))
 
 
+@pytest.mark.parametrize("T,nv", [(512, 3001), (512, -1), (511, 2999)])
+def test_layer_fp8_scale_copies(T, nv):
+    """fp8 token scales reach the routed positions by the gather pass (R = T*k >= 4096) or
+    by the quantising kernel's per-slot stores (below): both compared whole, with sentinel
+    rows and a workspace filled with NaN bytes beforehand."""
+    import grouped_gemm_histogram_amd as g
+    cfg = small_variant(get_config("deepseekv3_fp8"), T).replace(H=512, I=256, E=32, num_valid_rows=nv)
+    say(f"layer fp8 scale copies {cfg}: R={cfg.T * cfg.k}")
+    inp = generate(cfg, "cpu")
+    dev = inp.to(DEV)
+    need = g.forward_workspace_bytes(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, dev.w13.dtype)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    out, aux = g.forward(dev.x, dev.logits, dev.w13, dev.w2, cfg.k, cfg.num_valid_rows, cfg.renormalize,
+                         dev.w13_scale, dev.w2_scale, workspace=ws, return_aux=True)
+    torch.cuda.synchronize()
+    ref = olayer.forward(np32(inp.x), inp.logits.numpy(), _weights_host(inp), cfg.k,
+                         cfg.num_valid_rows, cfg.renormalize)
+    _check_routing(aux, ref)
+    got = np32(out)
+    dead = np.all(ref["out"] == 0, axis=1)
+    assert np.all(got[dead] == 0)
+    err = row_rel_err(got[~dead], ref["out"][~dead])
+    say(f"  max row-relative error {err:.3e} (tolerance {TOL[cfg.dtype]})")
+    assert err <= TOL[cfg.dtype]
+
+
 def test_layer_no_valid_rows():
     cfg = _small_cfg("gptoss20b_bf16").replace(num_valid_rows=0)
     inp = generate(cfg, "cpu").to(DEV)
