@@ -380,7 +380,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library has no "
               f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         return 2
 
