@@ -639,3 +639,22 @@ def test_combine(ydt, odt, H, k):
     assert np.all(got[dead] == 0)
     tol = 1e-2 if odt == torch.bfloat16 else 1e-5
     assert row_rel_err(got[~dead], ref[~dead]) <= tol
+
+
+def test_combine_y_beyond_mall():
+    """y larger than 256 MiB takes the launch with four column steps of loads in flight."""
+    T, k, E, H = 1024, 16, 20, 8704
+    R = T * k
+    assert R * H * 2 > 256 << 20
+    say(f"combine bf16 T={T} k={k} H={H} (y {R * H * 2 / 2**20:.0f} MiB)")
+    ids, w, off, sr, rp = _routing(T, E, k, R - 1000, 11)
+    V = int(off[-1])
+    y = torch.randn(R, H, generator=torch.Generator().manual_seed(12)).to(torch.bfloat16)
+    y[V:] = float("nan")
+    out = ops().unpermute_combine(y.to(DEV), torch.from_numpy(rp).to(DEV), torch.from_numpy(w).to(DEV),
+                                  torch.from_numpy(off).to(DEV), k, out_dtype=torch.bfloat16)
+    got = np32(out)
+    ref = olayer.combine(y.float().numpy(), rp, ids.reshape(-1), w.reshape(-1), T, k, E)
+    dead = (np.arange(T) * k) >= V
+    assert np.all(got[dead] == 0)
+    assert row_rel_err(got[~dead], ref[~dead]) <= 1e-2
