@@ -302,6 +302,8 @@ def _u8_to_fp8(a):
     (600, 600, 5, 512, 384, "silu_mul", "bf16"),
     (600, 480, 7, 384, 256, "none", "bf16"),
     (300, 0, 3, 256, 128, "silu_mul", "fp8"),
+    (600, 570, 5, 512, 128, "silu_mul", "fp8"),
+    (600, 590, 5, 384, 128, "none", "bf16"),
     # decode sizes (at most 8 rows per expert): 16-row tiles; fp8 output keeps 128-column tiles
     (40, 40, 6, 512, 384, "silu_mul", "bf16"),
     (40, 33, 6, 512, 384, "silu_mul", "f32"),
@@ -420,6 +422,10 @@ MULTI_TILE = [
     ("bf16", True, 4096, 4, 32, 1152, 1024),
     ("fp8", False, 16384, 1, 32, 1280, 2048),    # 128x256 tiles: ~32 x 4 x 5 tiles, 16 slices
     ("fp8", True, 4096, 4, 32, 1280, 2048),
+    # one and three 128-deep fp8 slices per tile (the pipeline's first and last slice
+    # coincide, or an odd count after the pairs), several tiles per workgroup
+    ("fp8", False, 16384, 1, 32, 1280, 128),
+    ("fp8", True, 4096, 4, 32, 1280, 384),
 ]
 
 
@@ -465,9 +471,9 @@ def test_grouped_gemm_multi_round_exact(dt, gathered, T, k, E, N, K):
     assert torch.equal(C.cpu().view(torch.int32), C2.cpu().view(torch.int32))
 
 
-# Launches of one, two and three 64-deep K slices with several tiles per workgroup: the
-# next tile's first slices are issued before the current tile's epilogue, here with fewer
-# slices per tile than LDS stages; E = 63, empty experts (the last among them), experts of
+# Launches of one, two and three 64-deep K slices with several tiles per workgroup: a
+# tile's first slices land in stages that follow on from the previous tile's, here with
+# fewer slices per tile than LDS stages; E = 63, empty experts (the last among them), experts of
 # exactly 256 and 512 rows, ragged output widths.  Integer operands: bit-exact against the
 # oracle.
 SHORT_K_CASES = [
