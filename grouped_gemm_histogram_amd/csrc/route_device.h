@@ -13,6 +13,41 @@
 
 namespace moe {
 
+// (value, id) pairs ordered by value descending, then id ascending; -0.0 and +0.0 are
+// equal values.  This is a total order, so any reduction tree picks the same pair.
+__device__ __forceinline__ void keep_better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// One step of the arg-max within each 16-lane row: the pair held by the lane that the
+// DPP pattern names (lane ^ 1, lane ^ 2, the mirrored lane within 8, within 16).
+template <int kDppCtrl>
+__device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), kDppCtrl, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, kDppCtrl, 0xf, 0xf, false);
+  keep_better(bv, bi, ov, oi);
+}
+
+// Wave-wide arg-max; every lane gets the best pair.  Within each row of 16 lanes by DPP
+// moves (no LDS traffic), then across the four rows from their first lanes.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp_step<0xb1>(bv, bi);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+  argmax_dpp_step<0x4e>(bv, bi);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+  argmax_dpp_step<0x141>(bv, bi);   // row_half_mirror: the other quad of the 8
+  argmax_dpp_step<0x140>(bv, bi);   // row_mirror: the other 8 of the row
+  float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 16; r < kWave; r += 16)
+    keep_better(v, i, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r)),
+                __builtin_amdgcn_readlane(bi, r));
+  bv = v;
+  bi = i;
+}
+
 // Token t's k ids and weights (flat rows t*k .. t*k+k-1; rows at or past valid_rows,
 // when valid_rows >= 0, become sentinel id E with weight 0).  Called by a whole wave.
 template <int EPL>
@@ -44,15 +79,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if (j == 0) top = bv;
     if (lane == j) {
       my_val = bv;
