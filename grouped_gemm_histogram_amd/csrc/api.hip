@@ -8,6 +8,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "launch.h"
 #include "moe.h"
 
@@ -80,7 +82,7 @@ FwdLayout fwd_layout(long long T, long long H, long long I, int E, int k, moe_dt
   L.offsets = take((E + 1) * 4);
   L.sorted = take(R * 4);
   L.rowpos = take(R * 4);
-  L.offws = take(moe::build_offsets_workspace_bytes(R, E));
+  L.offws = take(std::max(moe::build_offsets_workspace_bytes(R, E), moe::route_offsets_workspace_bytes(T, E)));
   L.xp = take(fp8 ? T * H : 0);                     // fp8: quantised token rows
   L.xps = take(fp8 ? T * (H / 128) * 4 : 0);
   L.xpsr = take(fp8 ? R * (H / 128) * 4 : 0);          // the same scales at the routed rows
@@ -407,6 +409,18 @@ moe_status_t moe_forward(const void* x, moe_dtype_t x_dtype, const float* router
                       "route_offsets_single")))
       return s;
     if ((s = mark(1))) return s;
+  } else if (T > 0) {
+    // routing with the per-chunk histograms (the routing stage), then the per-bin scan
+    // over chunks and the scatter (the offsets stage)
+    if ((s = launched(moe::launch_route_hist(router_logits, (int)T, E, k, num_valid_rows, renormalize ? 1 : 0,
+                                             ids, wts, ws + L.offws, as_stream(stream)),
+                      "route_hist")))
+      return s;
+    if ((s = mark(1))) return s;
+    if ((s = launched(moe::launch_offsets_from_hist(ids, (int)T, E, k, offs, sorted, rowpos, ws + L.offws,
+                                                    as_stream(stream)),
+                      "offsets_from_hist")))
+      return s;
   } else {
     if ((s = moe_route_topk(router_logits, T, E, k, num_valid_rows, renormalize, ids, wts, stream)))
       return s;

@@ -15,6 +15,16 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, long long
 hipError_t launch_route_offsets_single(const float* logits, int T, int E, int k, long long valid_rows, int renorm,
                                        int* ids, float* weights, int* offsets, int* sorted_rows, int* row_pos,
                                        hipStream_t stream);
+// T >= 1, k <= 16: routing with per-chunk histograms in one launch (launch_route_hist),
+// then a per-bin scan over chunks and the scatter (launch_offsets_from_hist, on the same
+// workspace): three launches instead of four, with the outputs of launch_route_topk
+// followed by launch_build_offsets.  workspace: route_offsets_workspace_bytes(T, E) bytes,
+// 4-byte aligned.
+size_t route_offsets_workspace_bytes(long long T, int E);
+hipError_t launch_route_hist(const float* logits, int T, int E, int k, long long valid_rows, int renorm,
+                             int* ids, float* weights, void* workspace, hipStream_t stream);
+hipError_t launch_offsets_from_hist(const int* ids, int T, int E, int k, int* offsets, int* sorted_rows,
+                                    int* row_pos, void* workspace, hipStream_t stream);
 size_t build_offsets_workspace_bytes(long long R, int E);
 // the allocation-free variant's static scratch: its size, and this device's address of it
 size_t build_offsets_noalloc_capacity();

@@ -18,7 +18,9 @@
 //               row's rank among equal ids in the same 64 comes from ballots
 //               over the id bits (lanes with equal ids), so ties keep flat
 //               order without any atomic.
-// A launch of at most one chunk (decode sizes) runs all three in one workgroup.
+// A launch of at most one chunk (decode sizes) runs all three in one workgroup.  The
+// layer above decode sizes counts the histogram in its routing launch instead (chunks
+// of 16 tokens, stored bin-major), then scans each bin over the chunks and scatters.
 
 #include <mutex>
 
@@ -205,6 +207,183 @@ __global__ __launch_bounds__(1024) void route_offsets_single_kernel(const float*
     route_token<EPL>(logits, t, E, k, valid_rows, renorm, ids, weights);
   __syncthreads();
   offsets_single(ids, T * k, E, id_bits, offsets, sorted_rows, row_pos);
+}
+
+// ---- The layer's path above decode sizes: routing fused with the histogram.
+//
+// A workgroup of kRouteWaves waves routes kRouteWaves consecutive tokens (a wave each), so
+// its chunk is those tokens' kRouteWaves*k flat rows.  It counts the chunk's bins in LDS as
+// the ids are written and stores the counts bin-major, hist[b * nchunks + c], so that the
+// per-bin scan over chunks reads contiguous words.  Then one workgroup per bin scans its
+// counts over the chunks (in place, exclusive) and stores the bin's total, and one wave
+// per chunk places the chunk's rows, starting from the exclusive scan of the bin totals
+// (which every such wave computes for itself; chunk 0's wave also stores it as offsets).
+// Same outputs as routing followed by the three-launch offsets above, one launch fewer.
+constexpr int kRouteWaves = 16;
+
+template <int EPL>
+__global__ __launch_bounds__(kRouteWaves * kWave) void route_hist_kernel(
+    const float* __restrict__ logits, int T, int E, int k, long long valid_rows, int renorm,
+    int* __restrict__ ids, float* __restrict__ weights, int nchunks, int* __restrict__ hist) {
+  __shared__ int h[kMaxBins];
+  const int nb = E + 1;
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRouteWaves + (int)(threadIdx.x >> 6);
+  if (t < T) {
+    const int id = route_token<EPL>(logits, t, E, k, valid_rows, renorm, ids, weights);
+    if (id >= 0) atomicAdd(&h[id], 1);   // id is in [0, E]: E for a sentinel row
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[(size_t)i * nchunks + blockIdx.x] = h[i];
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// One workgroup per bin b: hist[b][0, nchunks) becomes its exclusive scan over chunks, and
+// tot[b] the bin's total.  kScanPer consecutive chunks per thread per pass.
+constexpr int kBinScanThreads = 256;
+constexpr int kScanPer = 4;
+__global__ __launch_bounds__(kBinScanThreads) void scan_bins_kernel(int* __restrict__ hist, int nchunks,
+                                                                   int* __restrict__ tot) {
+  __shared__ int wsum[kBinScanThreads / kWave];
+  int* row = hist + (size_t)blockIdx.x * nchunks;
+  const int lane = lane_id(), wv = (int)(threadIdx.x >> 6);
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += kBinScanThreads * kScanPer) {
+    const int cb = c0 + (int)threadIdx.x * kScanPer;
+    int v[kScanPer], s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      v[i] = (cb + i < nchunks) ? row[cb + i] : 0;
+      s += v[i];
+    }
+    const int incl = wave_inclusive_scan(s);
+    if (lane == kWave - 1) wsum[wv] = incl;
+    __syncthreads();
+    int before = carry, pass = 0;
+#pragma unroll
+    for (int w = 0; w < kBinScanThreads / kWave; ++w) {
+      if (w < wv) before += wsum[w];
+      pass += wsum[w];
+    }
+    int run = before + incl - s;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      if (cb + i < nchunks) row[cb + i] = run;
+      run += v[i];
+    }
+    carry += pass;
+    __syncthreads();   // wsum is rewritten by the next pass
+  }
+  if (threadIdx.x == 0) tot[blockIdx.x] = carry;
+}
+
+// One wave per chunk of chunk_rows (<= kSteps * 64) flat rows.  hist holds each (bin,
+// chunk)'s first place within its bin, tot the bin totals.
+template <int kSteps>
+__global__ __launch_bounds__(64) void scatter_binmajor_kernel(const int* __restrict__ ids, int R, int E,
+                                                              int id_bits, int chunk_rows, int nchunks,
+                                                              const int* __restrict__ hist,
+                                                              const int* __restrict__ tot,
+                                                              int* __restrict__ offsets,
+                                                              int* __restrict__ sorted_rows,
+                                                              int* __restrict__ row_pos) {
+  __shared__ int cursor[kMaxBins];
+  const int nb = E + 1;
+  const int lane = lane_id();
+  const int c = blockIdx.x;
+  // bin bases: the exclusive scan of the totals over bins, lane l summing a run of
+  // consecutive bins
+  const int per = (nb + kWave - 1) / kWave;
+  const int b0 = lane * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) s += tot[b0 + i];
+  int base = wave_inclusive_scan(s) - s;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b >= nb) break;
+    cursor[b] = base + hist[(size_t)b * nchunks + c];
+    if (c == 0) offsets[b] = base;   // offsets[E] = valid rows
+    base += tot[b];
+  }
+  __syncthreads();
+  const int r0 = c * chunk_rows;
+  scatter_rows<kSteps>(ids, r0, min(R, r0 + chunk_rows), E, id_bits, cursor, sorted_rows, row_pos);
+}
+
+size_t route_offsets_workspace_bytes(long long T, int E) {
+  const long long nchunks = (T + kRouteWaves - 1) / kRouteWaves;
+  return (size_t)((nchunks > 0 ? nchunks : 1) + 1) * (size_t)(E + 1) * sizeof(int);
+}
+
+namespace {
+struct RouteChunks {
+  int nchunks, chunk, id_bits;
+  int* hist;
+  int* tot;
+};
+RouteChunks route_chunks(int T, int E, int k, void* workspace) {
+  RouteChunks c;
+  c.nchunks = (T + kRouteWaves - 1) / kRouteWaves;
+  c.chunk = kRouteWaves * k;
+  c.hist = static_cast<int*>(workspace);
+  c.tot = c.hist + (size_t)c.nchunks * (E + 1);
+  c.id_bits = 1;
+  while ((1 << c.id_bits) <= E) ++c.id_bits;   // bins 0..E need id_bits bits
+  return c;
+}
+bool route_chunks_ok(int T, int E, int k) {
+  return T >= 1 && k >= 1 && k * kRouteWaves <= 4 * kWave && E >= 1 && E <= kMaxBins - 1;
+}
+}  // namespace
+
+hipError_t launch_route_hist(const float* logits, int T, int E, int k, long long valid_rows, int renorm,
+                             int* ids, float* weights, void* workspace, hipStream_t stream) {
+  if (!route_chunks_ok(T, E, k)) return hipErrorInvalidValue;
+  const RouteChunks c = route_chunks(T, E, k, workspace);
+#define MOE_ROUTE_HIST_CASE(EPL)                                                                             \
+  hipLaunchKernelGGL(route_hist_kernel<EPL>, dim3(c.nchunks), dim3(kRouteWaves * kWave), 0, stream, logits, \
+                     T, E, k, valid_rows, renorm, ids, weights, c.nchunks, c.hist);                          \
+  break;
+  switch ((E + kWave - 1) / kWave) {
+    case 1: MOE_ROUTE_HIST_CASE(1)
+    case 2: MOE_ROUTE_HIST_CASE(2)
+    case 3: case 4: MOE_ROUTE_HIST_CASE(4)
+    case 5: case 6: case 7: case 8: MOE_ROUTE_HIST_CASE(8)
+    default: MOE_ROUTE_HIST_CASE(16)
+  }
+#undef MOE_ROUTE_HIST_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_offsets_from_hist(const int* ids, int T, int E, int k, int* offsets, int* sorted_rows,
+                                    int* row_pos, void* workspace, hipStream_t stream) {
+  if (!route_chunks_ok(T, E, k)) return hipErrorInvalidValue;
+  const RouteChunks c = route_chunks(T, E, k, workspace);
+  hipLaunchKernelGGL(scan_bins_kernel, dim3(E + 1), dim3(kBinScanThreads), 0, stream, c.hist, c.nchunks, c.tot);
+#define MOE_SCATTER_BM(STEPS)                                                                               \
+  hipLaunchKernelGGL(scatter_binmajor_kernel<STEPS>, dim3(c.nchunks), dim3(kWave), 0, stream, ids, T * k, E, \
+                     c.id_bits, c.chunk, c.nchunks, c.hist, c.tot, offsets, sorted_rows, row_pos);
+  if (c.chunk <= kWave) {
+    MOE_SCATTER_BM(1)
+  } else if (c.chunk <= 2 * kWave) {
+    MOE_SCATTER_BM(2)
+  } else {
+    MOE_SCATTER_BM(4)
+  }
+#undef MOE_SCATTER_BM
+  return hipGetLastError();
 }
 
 // Scratch of the allocation-free entry point: one array per GPU, in the code object's

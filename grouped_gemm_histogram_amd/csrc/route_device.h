@@ -50,8 +50,10 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
 
 // Token t's k ids and weights (flat rows t*k .. t*k+k-1; rows at or past valid_rows,
 // when valid_rows >= 0, become sentinel id E with weight 0).  Called by a whole wave.
+// Returns, on lane j < k, the id stored for slot j (E for a sentinel row); -1 on the
+// other lanes.
 template <int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+__device__ __forceinline__ int route_token(const float* __restrict__ logits, int t, int E, int k,
                                             long long valid_rows, int renorm, int* __restrict__ ids,
                                             float* __restrict__ weights) {
   const int lane = lane_id();
@@ -99,12 +101,15 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
       if (lane + kWave * i < E) s += expf(v[i] - top);
     denom = wave_sum(s);
   }
+  int stored = -1;
   if (lane < k) {
     const long long r = (long long)t * k + lane;
     const bool valid = valid_rows < 0 || r < valid_rows;
-    ids[r] = valid ? my_idx : E;
+    stored = valid ? my_idx : E;
+    ids[r] = stored;
     weights[r] = valid ? ex / denom : 0.0f;
   }
+  return stored;
 }
 
 }  // namespace moe

@@ -131,6 +131,46 @@ def test_layer_fp8_scale_copies(T, nv):
     assert err <= TOL[cfg.dtype]
 
 
+# Routing shapes of the layer path above decode sizes (routing and per-chunk histograms in one
+# launch, chunks of 16 tokens): token counts off the chunk size, one expert, 1024 experts,
+# k = 16 (256-row chunks), odd k (ragged 64-row steps), tied logits, partial and empty
+# valid-row prefixes; narrow widths keep the GEMMs cheap.
+ROUTING_SHAPES = [
+    # T, E, k, num_valid_rows, tied logits
+    (17, 1, 1, -1, False),
+    (1000, 1024, 16, -1, True),
+    (333, 65, 3, 500, False),
+    (4100, 8, 2, -1, True),
+    (20, 256, 16, 0, False),
+    (77, 40, 5, 301, True),
+    (130, 300, 9, -1, False),
+]
+
+
+@pytest.mark.parametrize("T,E,k,nv,ties", ROUTING_SHAPES)
+def test_layer_routing_shapes(T, E, k, nv, ties):
+    cfg = small_variant(get_config("gptoss20b_bf16"), T, "_route").replace(
+        H=128, I=128, E=E, k=k, num_valid_rows=nv)
+    say(f"layer routing shapes T={T} E={E} k={k} nv={nv} ties={ties}")
+    inp = generate(cfg, "cpu")
+    if ties:
+        lg = torch.round(inp.logits * 2) / 2
+        zero = lg == 0
+        lg[zero] = torch.where(torch.rand(int(zero.sum()), generator=torch.Generator().manual_seed(T)) < 0.5,
+                               -0.0, 0.0)
+        inp.logits = lg.contiguous()
+    dev = inp.to(DEV)
+    out, aux = _run(dev)
+    ref = olayer.forward(np32(inp.x), inp.logits.numpy(), _weights_host(inp), cfg.k,
+                         cfg.num_valid_rows, cfg.renormalize)
+    _check_routing(aux, ref)
+    got = np32(out)
+    dead = np.all(ref["out"] == 0, axis=1)
+    assert np.all(got[dead] == 0)
+    if (~dead).any():
+        assert row_rel_err(got[~dead], ref["out"][~dead]) <= TOL[cfg.dtype]
+
+
 def test_layer_no_valid_rows():
     cfg = _small_cfg("gptoss20b_bf16").replace(num_valid_rows=0)
     inp = generate(cfg, "cpu").to(DEV)
