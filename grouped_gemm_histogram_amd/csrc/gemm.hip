@@ -867,6 +867,21 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
           // one slice; LAST = no next slice (no barrier, no reads of it).  The last
           // slice is peeled off so that the body is straight-line code and the
           // compiler's LDS wait counts stay exact.
+          // Within an MFMA row, one LDS fragment read after each MFMA (then the row's
+          // remaining MFMAs) rather than the reads as a group before the MFMAs, so that the
+          // LDS sees an even stream of reads (gpt-oss-20b and Mixtral-8x7B layers 0.3-1.7%
+          // faster, outputs bit-identical; two MFMAs per read and reads after MFMA pairs
+          // measured slower).  Instructions outside these classes (the direct loads) are
+          // placed by the scheduler.
+          auto interleave_row = []() MOE_INLINE {
+            constexpr int kR = SNB / SM + 1, kM = SNB, kI = kR < kM ? kR : kM;
+#pragma unroll
+            for (int q = 0; q < kI; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kM - kI, 0);
+          };
           auto body = [&](int kt, auto last_tag) MOE_INLINE {
             constexpr bool LAST = decltype(last_tag)::value;
             const bool tail = LAST && has_tail;
@@ -883,6 +898,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
                 for (int j = 0; j < Cfg::kDmaPerSlice; ++j)
                   if (j * SM / Cfg::kDmaPerSlice == t) issue_one(j, kt + ST - 1, stn);
               }
+              interleave_row();
               __builtin_amdgcn_sched_barrier(0);
             }
             const int st1 = (st == ST - 1) ? 0 : st + 1;
@@ -896,6 +912,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_kernel(GemmArgs args
             for (int t = 0; t < SM; ++t) {
               if constexpr (!LAST) read_range(st1, 0, fa0, fw0, t * SNB / SM, (t + 1) * SNB / SM, t, t + 1);
               mma_row(t, fa1, fw1, keep1);
+              interleave_row();
               __builtin_amdgcn_sched_barrier(0);
             }
             st = st1;
