@@ -157,32 +157,47 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   scatter_rows<kSteps>(ids, r0, min(R, r0 + chunk), E, id_bits, cursor, sorted_rows, row_pos);
 }
 
-// R <= kChunk: histogram, bin scan and scatter by one workgroup of 1024 threads.
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// R <= kChunk: the histogram by the whole workgroup (LDS atomics), then the bin scan and
+// the scatter by its first wave alone (lane runs of consecutive bins and a wave scan), so
+// that one workgroup barrier suffices.
 __device__ __forceinline__ void offsets_single(const int* __restrict__ ids, int R, int E, int id_bits,
                                                int* __restrict__ offsets, int* __restrict__ sorted_rows,
                                                int* __restrict__ row_pos) {
-  __shared__ int tot[2][kMaxBins + 1];
+  __shared__ int cnt[kMaxBins];
   const int nb = E + 1;
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) tot[0][b] = 0;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) cnt[b] = 0;
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&tot[0][bin_of(ids[r], E)], 1);
+  for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&cnt[bin_of(ids[r], E)], 1);
   __syncthreads();
-  // Hillis-Steele inclusive scan over the nb bin counts
-  int src = 0;
-  for (int d = 1; d < nb; d <<= 1) {
-    for (int b = threadIdx.x; b < nb; b += blockDim.x)
-      tot[src ^ 1][b] = tot[src][b] + (b >= d ? tot[src][b - d] : 0);
-    __syncthreads();
-    src ^= 1;
+  if (threadIdx.x >= kWave) return;
+  // exclusive bases: offsets[b], and (in place) the scatter cursors
+  const int per = (nb + kWave - 1) / kWave;
+  const int b0 = lane_id() * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) s += cnt[b0 + i];
+  int base = wave_inclusive_scan(s) - s;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b >= nb) break;
+    const int c = cnt[b];
+    offsets[b] = base;   // offsets[E] = valid rows
+    cnt[b] = base;
+    base += c;
   }
-  // exclusive bases: offsets[b], and the scatter cursors (in the other buffer)
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-    const int base = (b == 0) ? 0 : tot[src][b - 1];
-    offsets[b] = base;
-    tot[src ^ 1][b] = base;
-  }
-  __syncthreads();
-  if (threadIdx.x < kWave) scatter_rows<kChunk / kWave>(ids, 0, R, E, id_bits, tot[src ^ 1], sorted_rows, row_pos);
+  __builtin_amdgcn_wave_barrier();
+  scatter_rows<kChunk / kWave>(ids, 0, R, E, id_bits, cnt, sorted_rows, row_pos);
 }
 
 __global__ __launch_bounds__(1024) void offsets_single_kernel(const int* __restrict__ ids, int R, int E,
@@ -236,17 +251,6 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_hist_kernel(
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[(size_t)i * nchunks + blockIdx.x] = h[i];
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
 }
 
 // One workgroup per bin b: hist[b][0, nchunks) becomes its exclusive scan over chunks, and
