@@ -134,7 +134,8 @@ def test_layer_fp8_scale_copies(T, nv):
 # Routing shapes of the layer path above decode sizes (routing and per-chunk histograms in one
 # launch, chunks of 16 tokens): token counts off the chunk size, one expert, 1024 experts,
 # k = 16 (256-row chunks), odd k (ragged 64-row steps), tied logits, partial and empty
-# valid-row prefixes; narrow widths keep the GEMMs cheap.
+# valid-row prefixes, and more chunks than one pass of the per-bin scan covers; narrow
+# widths keep the GEMMs cheap.
 ROUTING_SHAPES = [
     # T, E, k, num_valid_rows, tied logits
     (17, 1, 1, -1, False),
@@ -144,6 +145,9 @@ ROUTING_SHAPES = [
     (20, 256, 16, 0, False),
     (77, 40, 5, 301, True),
     (130, 300, 9, -1, False),
+    # more than 1024 chunks of 16 tokens: the per-bin scan runs several passes with a carry
+    (20000, 64, 2, -1, False),
+    (40000, 1024, 16, 300000, True),
 ]
 
 
