@@ -11,7 +11,7 @@
 //   1. hist:    one workgroup per chunk of rows (256 rows up to 16384 rows, else
 //               1024), LDS histogram over E+1 bins.
 //   2. scan:    one workgroup; per-bin exclusive scan over chunks (a thread
-//               per bin), then the exclusive scan over bins -> offsets; a
+//               per bin), then the exclusive scan over bins (first wave) -> offsets; a
 //               chunk's cursor for a bin is its place in the bin plus the bin's
 //               offset.
 //   3. scatter: one wave per chunk walks its rows in order, 64 at a time; a
@@ -56,17 +56,29 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, 
   for (int i = threadIdx.x; i < nb; i += blockDim.x) chunk_hist[(size_t)blockIdx.x * nb + i] = h[i];
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
 // One workgroup of kScanThreads threads.  chunk_hist [nchunks][E+1] becomes, in place,
 // each (chunk, bin)'s first position within its bin (the exclusive scan of the bin's
 // counts over chunks); offsets[b] is the bin's base (the exclusive scan of the bin
 // totals), which the scatter adds.  A thread scans one bin over the chunks, loading up to
 // kScanBatch chunk counts at once (neighbouring threads read neighbouring bins); a small
-// workgroup leaves each thread the registers for the whole batch.
+// workgroup leaves each thread the registers for the whole batch.  The first wave then
+// scans the bin totals (lane runs of consecutive bins and a wave scan).
 constexpr int kScanThreads = 256;
 constexpr int kScanBatch = 64;
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int* __restrict__ chunk_hist, int nchunks,
                                                             int E, int* __restrict__ offsets) {
-  __shared__ int tot[2][kMaxBins + 1];
+  __shared__ int tot[kMaxBins];
   const int nb = E + 1;
   for (int b = threadIdx.x; b < nb; b += blockDim.x) {
     int run = 0;
@@ -81,19 +93,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int* __restrict__ ch
         run += v[i];
       }
     }
-    tot[0][b] = run;
+    tot[b] = run;
   }
   __syncthreads();
-  // Hillis-Steele inclusive scan over the nb bin totals.
-  int src = 0;
-  for (int d = 1; d < nb; d <<= 1) {
-    for (int b = threadIdx.x; b < nb; b += blockDim.x)
-      tot[src ^ 1][b] = tot[src][b] + (b >= d ? tot[src][b - d] : 0);
-    __syncthreads();
-    src ^= 1;
+  if (threadIdx.x >= kWave) return;
+  const int per = (nb + kWave - 1) / kWave;
+  const int b0 = lane_id() * per;
+  int s = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nb) s += tot[b0 + i];
+  int base = wave_inclusive_scan(s) - s;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b >= nb) break;
+    offsets[b] = base;   // offsets[E] = valid rows
+    base += tot[b];
   }
-  for (int b = threadIdx.x; b < nb; b += blockDim.x)
-    offsets[b] = (b == 0) ? 0 : tot[src][b - 1];   // offsets[E] = valid rows
 }
 
 // One wave places rows [r0, r1) (at most kSteps * 64 rows) in order; cursor[b] (LDS)
@@ -155,17 +170,6 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ ids
   constexpr int chunk = kSteps * kWave;
   const int r0 = blockIdx.x * chunk;
   scatter_rows<kSteps>(ids, r0, min(R, r0 + chunk), E, id_bits, cursor, sorted_rows, row_pos);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
 }
 
 // R <= kChunk: the histogram by the whole workgroup (LDS atomics), then the bin scan and
