@@ -211,6 +211,10 @@ DECODE = [
     # fp8: decode tiles with f32 h quantised in a second pass
     ("deepseekv3_fp8", 4, dict(H=512, I=256, E=32)),
     ("deepseekv3_fp8", 1, {}),
+    # sentinel rows in the one-launch routing + offsets path: a valid prefix ending inside a
+    # token's slots, and no valid row at all
+    ("gptoss20b_bf16", 8, dict(num_valid_rows=13)),
+    ("deepseekv3_fp8", 4, dict(H=512, I=256, E=32, num_valid_rows=0)),
 ]
 
 
@@ -227,6 +231,8 @@ def test_layer_decode_sizes(name, T, kw):
     _check_routing(aux, ref)
     if name.startswith("mixtral"):
         assert np.diff(ref["offsets"]).max() > 16          # the skew case covers several m-tiles
+    dead = np.all(ref["out"] == 0, axis=1)                 # tokens with no valid row: exact zeros
+    assert np.all(np32(out)[dead] == 0)
     err = row_rel_err(np32(out), ref["out"])
     say(f"  max row-relative error {err:.3e}")
     assert err <= TOL[cfg.dtype]
